@@ -1,0 +1,222 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one causal prefill over the stress workload (batch 4, 16 heads,
+N = 2048, d = 128, bf16, 1 % of Q/K rows x20) followed by one paged decode over
+64 sequences (context lengths uniform in [512, 8192], 32 query / 8 KV heads,
+d = 128, bf16 KV cache in 16-token blocks, shuffled block table).  Inputs are
+synthetic (seeded) and resident in device memory before timing starts.
+
+Prints one JSON line:
+  value          prefill TFLOP/s (algorithmic FLOP / mean prefill kernel time)
+  roofline       prefill kernel against the dense bf16 matrix-core peak
+  decode         decode GB/s (algorithmic K/V bytes / mean decode time, split +
+                 combine kernels) and its roofline against HBM bandwidth
+  cpu_baseline   the fp64 CPU oracle timed on the host on a bounded sample
+Kernel times come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain 1 GiB copies, for counters
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+METRIC = "prefill attention TFLOP/s (% MFMA peak) + paged decode GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_attention_34_amd", "csrc")
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch measured with counters, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one kernel family only (for profiling)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """Plain device copies of a known size (1 GiB), for scaling HBM counters."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def cpu_baseline(pre, dec, dec_bytes, pre_flops):
+    """Time the fp64 oracle on a bounded sample of the same workloads."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = (x.float().numpy() for x in (pre.q, pre.k, pre.v))
+    # prefill sample: the whole stress workload (64 (batch, head) pairs)
+    t0 = time.perf_counter()
+    oracle.sdpa(q, k, v, pre.scale, True)
+    t_pre = time.perf_counter() - t0
+    flops_sample = pre_flops
+    # decode sample: all 64 sequences
+    ns = dec.q.shape[0]
+    t0 = time.perf_counter()
+    oracle.paged_decode(dec.q[:ns].double().numpy(), dec.k_cache.float().numpy(),
+                        dec.v_cache.float().numpy(), dec.block_table[:ns].numpy(),
+                        dec.context_lens[:ns].numpy(), dec.block_size, dec.scale)
+    t_dec = time.perf_counter() - t0
+    bytes_sample = int(dec.context_lens[:ns].to(torch.int64).sum()) * 8 * 128 * 2 * 2
+    return {
+        "value": flops_sample / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": "one pass of each workload: prefill B=4 H=16 N=2048 causal (%.1f s), "
+                  "decode of all 64 sequences (%.1f s)" % (t_pre, t_dec),
+        "decode_value": bytes_sample / t_dec / 1e9, "decode_unit": "GB/s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import exact_attention_34_amd as ea
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pre = workloads.prefill_config(2)
+    B, N, Hq, d = pre.q.shape
+    pre_flops = workloads.prefill_flops(B, N, N, Hq, d, True)
+    q, k, v = (x.to(dev) for x in (pre.q, pre.k, pre.v))
+    o = torch.empty_like(q)
+
+    dec = workloads.decode_config4(nan_fill=True)
+    dq = dec.q.to(dev)
+    kc, vc = dec.k_cache.to(dev), dec.v_cache.to(dev)
+    tab, ctx = dec.block_table.to(dev), dec.context_lens.to(dev)
+    mcl = 8192
+    dout = torch.empty_like(dq)
+    ws = torch.empty(max(1, ea.paged_attn_decode_workspace_size(dq.shape[0], dq.shape[1], 128,
+                                                                mcl)),
+                     dtype=torch.uint8, device=dev)
+    dec_bytes = workloads.decode_bytes(dec.context_lens.numpy(), 8, 128)
+
+    run_pre = args.only in (None, "prefill")
+    run_dec = args.only in (None, "decode")
+
+    def step(ev=None):
+        if run_pre:
+            if ev is not None:
+                ev[0].record()
+            ea.attn_fwd(q, k, v, causal=True, scale=pre.scale, out=o)
+            if ev is not None:
+                ev[1].record()
+        if run_dec:
+            if ev is not None:
+                ev[2].record()
+            ea.paged_attn_decode(dq, kc, vc, tab, ctx, max_context_len=mcl, scale=dec.scale,
+                                 out=dout, workspace=ws)
+            if ev is not None:
+                ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events])) if run_pre else None
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if run_dec else None
+
+    res = {
+        "metric": METRIC,
+        "value": None, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "causal prefill B=4 Hq=Hkv=16 N=2048 d=128 bf16 (1% Q/K rows x20) "
+                        "+ paged decode 64 seqs ctx~U[512,8192] Hq=32 Hkv=8 d=128 bf16 "
+                        "block 16 shuffled table",
+            "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
+        },
+    }
+    if run_pre:
+        tflops = pre_flops / (pre_ms * 1e-3) / 1e12
+        traffic = load_traffic("attn_fwd_mfma_kernel")
+        res["value"] = tflops
+        res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                           "traffic": traffic, "kernel": "attn_fwd_mfma_kernel<bf16,128,causal>",
+                           "flop_per_launch": pre_flops, "mean_ms": pre_ms}
+    if run_dec:
+        gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+        res["decode"] = {
+            "value": gbs, "unit": "GB/s", "mean_ms": dec_ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": load_traffic("paged_decode_split_kernel"),
+                         "kernel": "paged_decode_split_kernel + paged_decode_combine_kernel",
+                         "bytes_per_launch": dec_bytes},
+        }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(pre, dec, dec_bytes, pre_flops)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

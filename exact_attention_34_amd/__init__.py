@@ -1,0 +1,197 @@
+"""Exact attention for AMD MI355X (gfx950): Python binding of libattn.so.
+
+The binding only marshals arguments: it checks tensor shapes and dtypes,
+passes device pointers, strides and the current HIP stream to the C ABI
+declared in ``include/attn.h``, and turns error codes into exceptions.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  If ``libattn.so`` has not been built, every call raises.
+
+PyTorch provides device memory and streams only.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from . import build as _build
+
+__all__ = [
+    "AttnError", "lib", "abi_version", "attn_fwd", "paged_attn_decode",
+    "paged_attn_decode_workspace_size", "LIB_PATH",
+]
+
+LIB_PATH = _build.LIB_PATH
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+ERROR_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+               4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from libattn.so (``code`` is the ATTN_ERR_* value)."""
+
+    def __init__(self, code, message):
+        super().__init__("%s: %s" % (ERROR_NAMES.get(code, code), message))
+        self.code = code
+
+
+_LIB = None
+_I64x3 = ctypes.c_int64 * 3
+
+
+def lib():
+    """The loaded library (ctypes.CDLL) with argument types declared."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libattn.so is not built (%s); run "
+                           "`python -m exact_attention_34_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    L.attn_abi_version.restype = i32
+    L.attn_abi_version.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_fwd.restype = i32
+    L.attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp,
+                           i32, i32, i32, i32, i32, i32,
+                           i64p, i64p, i64p, i64p, f32, i32, vp]
+    L.paged_attn_decode_workspace_size.restype = ctypes.c_size_t
+    L.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.paged_attn_decode.restype = i32
+    L.paged_attn_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, vp, ctypes.c_size_t, vp]
+    _LIB = L
+    return L
+
+
+def abi_version():
+    return lib().attn_abi_version()
+
+
+def _check(code):
+    if code != 0:
+        raise AttnError(code, lib().attn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _strides3(t):
+    if t.stride(-1) != 1:
+        raise ValueError("the head_dim axis must have stride 1")
+    return _I64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=False):
+    """Exact attention O = softmax(Q K^T * scale) V on the GPU.
+
+    ``q``: ``[B][Nq][Hq][d]``; ``k``, ``v``: ``[B][Nk][Hkv][d]`` (any strides
+    with the last axis contiguous), one dtype among float32/float16/bfloat16,
+    on one GPU.  ``scale`` defaults to ``1/sqrt(d)``.  ``causal`` applies the
+    bottom-right aligned mask.  ``out`` (same shape as ``q``) and ``lse``
+    (``[B][Hq][Nq]`` float32, contiguous) are optional preallocated outputs;
+    with ``return_lse`` the log-sum-exp is computed and returned too.
+    The call is asynchronous on the current stream.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B][N][H][d]")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype among float32, float16, bfloat16")
+    B, Nq, Hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B][Nk][Hkv][d] matching q")
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B][Hq][Nq] tensor")
+    for t in (q, k, v, out):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must be on the same GPU")
+    code = lib().attn_fwd(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                          B, Nq, Nk, Hq, Hkv, d,
+                          _strides3(q), _strides3(k), _strides3(v), _strides3(out),
+                          float(scale), int(bool(causal)), _stream(q.device))
+    _check(code)
+    if return_lse:
+        return out, lse
+    return out
+
+
+def paged_attn_decode_workspace_size(num_seqs, h_q, head_dim, max_context_len):
+    """Bytes of workspace :func:`paged_attn_decode` needs (0 if none)."""
+    return int(lib().paged_attn_decode_workspace_size(num_seqs, h_q, head_dim, max_context_len))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                      scale=None, out=None, lse=None, workspace=None, return_lse=False):
+    """Single-token decode over a paged KV cache.
+
+    ``q``: ``[S][Hq][d]``; ``k_cache``, ``v_cache``:
+    ``[num_blocks][Hkv][16][d]`` (contiguous, float16 or bfloat16);
+    ``block_table``: ``[S][max_blocks_per_seq]`` int32; ``context_lens``:
+    ``[S]`` int32, each at most ``max_context_len`` (a host int).  The
+    workspace is allocated from torch's caching allocator when not given.
+    Asynchronous on the current stream.
+    """
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [S][Hq][d] and the caches [blocks][Hkv][bs][d]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype \
+            or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share float16 or bfloat16")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_table and context_lens must be int32")
+    for t in (q, k_cache, v_cache, block_table, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must be on the same GPU")
+    S, Hq, d = q.shape
+    NB, Hkv, bs, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim mismatch")
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_table must be [S][max_blocks] and context_lens [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (S, Hq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [S][Hq] tensor")
+    need = paged_attn_decode_workspace_size(S, Hq, d, int(max_context_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = lib().paged_attn_decode(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse),
+                                   S, Hq, Hkv, d, bs, block_table.shape[1], int(max_context_len),
+                                   NB, float(scale), _ptr(workspace), ws_bytes,
+                                   _stream(q.device))
+    _check(code)
+    if return_lse:
+        return out, lse
+    return out

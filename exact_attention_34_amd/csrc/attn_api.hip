@@ -1,0 +1,207 @@
+// C ABI of libattn.so (declared in include/attn.h): host-side validation and
+// dispatch.  Nothing here allocates device memory or synchronises.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/attn.h"
+#include "common.h"
+
+namespace attn {
+hipError_t launch_prefill(int dtype, int head_dim, bool causal, const FwdParams& p,
+                          hipStream_t stream);
+hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream);
+size_t decode_workspace_bytes(int num_seqs, int h_q, int head_dim, int max_context_len);
+int decode_max_parts(int max_context_len);
+}  // namespace attn
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("ATTN_DEBUG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+             int batch, int n_q, int n_k, int h_q, int h_kv, int head_dim,
+             const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+             const int64_t* o_stride, float softmax_scale, int causal, void* stream) {
+  try {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: dtype must be ATTN_F32, ATTN_F16 or ATTN_BF16");
+    if (batch < 0 || n_q < 0 || n_k < 0 || h_q < 0 || h_kv < 0 || head_dim < 0)
+      return fail(ATTN_ERR_SHAPE, "attn_fwd: sizes must be non-negative");
+    if (h_kv == 0 || (h_q % h_kv) != 0)
+      return fail(ATTN_ERR_SHAPE, "attn_fwd: h_q must be a positive multiple of h_kv");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head_dim must be 64 or 128");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, "attn_fwd: causal must be 0 or 1");
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+      return fail(ATTN_ERR_SHAPE, "attn_fwd: softmax_scale must be finite and positive");
+    if (batch == 0 || n_q == 0 || h_q == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr) return fail(ATTN_ERR_NULL, "attn_fwd: q and o must not be NULL");
+    if (n_k > 0 && (k == nullptr || v == nullptr))
+      return fail(ATTN_ERR_NULL, "attn_fwd: k and v must not be NULL");
+    if (q_stride == nullptr || k_stride == nullptr || v_stride == nullptr || o_stride == nullptr)
+      return fail(ATTN_ERR_NULL, "attn_fwd: stride arrays must not be NULL");
+    const int es = elem_size(dtype);
+    const void* ptrs[4] = {q, k, v, o};
+    for (const void* ptr : ptrs)
+      if (ptr != nullptr && !aligned16(ptr))
+        return fail(ATTN_ERR_ALIGN, "attn_fwd: q, k, v and o must be 16-byte aligned");
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return fail(ATTN_ERR_ALIGN, "attn_fwd: lse must be 4-byte aligned");
+    const int64_t* strides[4] = {q_stride, k_stride, v_stride, o_stride};
+    for (const int64_t* st : strides)
+      for (int i = 0; i < 3; ++i) {
+        if (st[i] < 0) return fail(ATTN_ERR_SHAPE, "attn_fwd: strides must be non-negative");
+        if ((st[i] * es) % 16 != 0)
+          return fail(ATTN_ERR_ALIGN, "attn_fwd: batch/sequence/head strides must be multiples of 16 bytes");
+      }
+
+    attn::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.qs_b = q_stride[0]; p.qs_n = q_stride[1]; p.qs_h = q_stride[2];
+    p.ks_b = k_stride[0]; p.ks_n = k_stride[1]; p.ks_h = k_stride[2];
+    p.vs_b = v_stride[0]; p.vs_n = v_stride[1]; p.vs_h = v_stride[2];
+    p.os_b = o_stride[0]; p.os_n = o_stride[1]; p.os_h = o_stride[2];
+    p.batch = batch;
+    p.n_q = n_q;
+    p.n_k = n_k;
+    p.h_q = h_q;
+    p.h_kv = h_kv;
+    p.group = h_q / h_kv;
+    p.scale_log2 = softmax_scale * attn::kLog2e;
+    if ((int64_t)((n_q + 63) / 64) * batch * h_q > (int64_t)1 << 31)
+      return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: problem too large for one launch");
+    if (debug_enabled())
+      std::fprintf(stderr, "[attn] attn_fwd dtype=%d b=%d nq=%d nk=%d hq=%d hkv=%d d=%d causal=%d\n",
+                   dtype, batch, n_q, n_k, h_q, h_kv, head_dim, causal);
+    hipError_t e = attn::launch_prefill(dtype, head_dim, causal != 0, p,
+                                        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, std::string("attn_fwd: launch failed: ") + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, "attn_fwd: unexpected host exception");
+  }
+}
+
+size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int head_dim, int max_context_len) {
+  return attn::decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len);
+}
+
+int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* context_lens, void* o,
+                      float* lse, int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                      int max_blocks_per_seq, int max_context_len, int num_blocks,
+                      float softmax_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  try {
+    g_last_error.clear();
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: dtype must be ATTN_F16 or ATTN_BF16");
+    if (num_seqs < 0 || h_q < 0 || h_kv < 0 || head_dim < 0 || block_size < 0 ||
+        max_blocks_per_seq < 0 || max_context_len < 0 || num_blocks < 0)
+      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: sizes must be non-negative");
+    if (h_kv == 0 || h_q == 0 || (h_q % h_kv) != 0)
+      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: h_q must be a positive multiple of h_kv");
+    if (h_q / h_kv > 16)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: at most 16 query heads per KV head");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: head_dim must be 64 or 128");
+    if (block_size != 16)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: block_size must be 16");
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: softmax_scale must be finite and positive");
+    if ((int64_t)max_blocks_per_seq * block_size < (int64_t)max_context_len)
+      return fail(ATTN_ERR_SHAPE,
+                  "paged_attn_decode: max_blocks_per_seq * block_size < max_context_len");
+    if (max_context_len > 0 && num_blocks == 0)
+      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: num_blocks must be positive");
+    if (num_seqs == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr || context_lens == nullptr)
+      return fail(ATTN_ERR_NULL, "paged_attn_decode: q, o and context_lens must not be NULL");
+    if (max_context_len > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
+      return fail(ATTN_ERR_NULL, "paged_attn_decode: k_cache, v_cache and block_table must not be NULL");
+    const void* ptrs[4] = {q, k_cache, v_cache, o};
+    for (const void* ptr : ptrs)
+      if (ptr != nullptr && !aligned16(ptr))
+        return fail(ATTN_ERR_ALIGN, "paged_attn_decode: q, caches and o must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+      return fail(ATTN_ERR_ALIGN, "paged_attn_decode: block_table, context_lens and lse must be 4-byte aligned");
+    const size_t need = attn::decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len);
+    if (need > 0) {
+      if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE,
+                    "paged_attn_decode: workspace of " + std::to_string(need) + " bytes required, got " +
+                        std::to_string(workspace_bytes));
+      if (!aligned16(workspace))
+        return fail(ATTN_ERR_ALIGN, "paged_attn_decode: workspace must be 16-byte aligned");
+    }
+    if ((int64_t)num_seqs > 65535 || h_kv > 65535)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: too many sequences or heads for one launch");
+
+    attn::DecodeParams p{};
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.o = o;
+    p.lse = lse;
+    p.num_seqs = num_seqs;
+    p.h_q = h_q;
+    p.h_kv = h_kv;
+    p.group = h_q / h_kv;
+    p.head_dim = head_dim;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_parts = attn::decode_max_parts(max_context_len);
+    p.scale_log2 = softmax_scale * attn::kLog2e;
+    if (need > 0) {
+      const int64_t slots = (int64_t)num_seqs * h_q * p.max_parts;
+      p.ws_o = static_cast<float*>(workspace);
+      p.ws_ml = p.ws_o + slots * head_dim;
+    }
+    if (debug_enabled())
+      std::fprintf(stderr, "[attn] paged_attn_decode dtype=%d seqs=%d hq=%d hkv=%d d=%d parts=%d\n",
+                   dtype, num_seqs, h_q, h_kv, head_dim, p.max_parts);
+    hipError_t e = attn::launch_decode(dtype, p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, std::string("paged_attn_decode: launch failed: ") + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, "paged_attn_decode: unexpected host exception");
+  }
+}
+
+}  // extern "C"

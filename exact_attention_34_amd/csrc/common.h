@@ -1,0 +1,116 @@
+// Shared device-side helpers for the gfx950 attention kernels: vector types,
+// matrix-core wrappers, 16-bit packing and launch parameter structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type traits: matrix-core products with fp32 accumulation and the
+// fp32 -> 16-bit round-to-nearest-even packing of two values into one dword.
+struct BF16 {
+  typedef __bf16 elem;
+  // 32x32x16: A is 32 rows x 16 k, B is 16 k x 32 columns; each lane holds 8
+  // consecutive k values of one row (A) / one column (B).
+  __device__ static inline f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  // widen the low / high 16-bit half of a dword to fp32 (exact)
+  __device__ static inline float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  __device__ static inline float hi(uint32_t w) {
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+  }
+};
+
+struct F16 {
+  typedef _Float16 elem;
+  __device__ static inline f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  __device__ static inline float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static inline float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
+// Join the low halves (lo16) / high halves (hi16) of two dwords: the result
+// holds a's half in bits 0..15 and b's half in bits 16..31.
+__device__ inline uint32_t join_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ inline uint32_t join_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (l xor 32).
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs_b, qs_n, qs_h;
+  int64_t ks_b, ks_n, ks_h;
+  int64_t vs_b, vs_n, vs_h;
+  int64_t os_b, os_n, os_h;
+  int batch, n_q, n_k, h_q, h_kv, group;
+  int n_qtiles;     // ceil(n_q / BM)
+  int num_items;    // n_qtiles * batch * h_q
+  int xcd_chunk;    // work items kept together on one XCD (0 = no remap)
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* o;
+  float* lse;
+  float* ws_o;    // [num_seqs][h_q][max_parts][head_dim]
+  float* ws_ml;   // [num_seqs][h_q][max_parts][2]  (max in log2 units, sum)
+  int num_seqs, h_q, h_kv, group, head_dim;
+  int max_blocks_per_seq, max_parts;
+  float scale_log2;
+};
+
+}  // namespace attn

@@ -1,0 +1,169 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact fused attention (prefill) and paged
+ * single-token decode for AMD MI355X (gfx950).
+ *
+ * What is computed.  Both entry points compute exact scaled-dot-product
+ * attention, O = softmax(Q K^T * scale) V, the definition given on the page
+ * "Other people's interview notes" (zzsy.me), question "explain
+ * FlashAttention", part 1.  It is evaluated in one fused, tiled pass with the
+ * online-softmax update of part 2 of the same answer (running row maximum m
+ * and running sum l, accumulated output rescaled by exp(m_old - m_new)), so
+ * the N x N score and probability matrices are never written to device
+ * memory (the codelogiq.de FAQ on FlashAttention-2 vs standard attention).
+ * Decode reads a PagedAttention-style KV cache through a block table, as the
+ * tutorial "Chapter 3 Advanced principles: performance model and numerical
+ * stability", section 3.0, describes (fixed-size KV blocks, a per-sequence
+ * table of block ids, shared prefixes expressed as repeated ids).
+ *
+ * Conventions the pages leave open, fixed here:
+ *   - grouped-query attention: query head h reads KV head h / (h_q / h_kv);
+ *   - the causal mask is bottom-right aligned: key j is visible to query row
+ *     i when j <= i + (n_k - n_q) (the usual lower triangle when n_q == n_k);
+ *   - a row with no visible key gets output 0 and log-sum-exp -inf;
+ *   - the log-sum-exp is in natural-log units;
+ *   - 16-bit outputs are rounded to nearest-even from fp32.
+ *
+ * Arithmetic.  16-bit inputs: products on the matrix cores with fp32
+ * accumulation; softmax statistics and the output accumulator in fp32; the
+ * probabilities are rounded to the input type before the P*V product.  fp32
+ * inputs: fp32 throughout.
+ *
+ * Ownership.  Every pointer is device memory owned by the caller.  The
+ * library never allocates or frees device memory, keeps no pointer after a
+ * call returns, and holds no mutable global state apart from a thread-local
+ * error message.  Calls are re-entrant.
+ *
+ * Asynchrony.  Calls only enqueue kernels on the given stream (a hipStream_t
+ * passed as void*; NULL means the null stream) and never synchronise.  A
+ * device-side fault caused by invalid device data (an out-of-range block id,
+ * a context length above the stated maximum) surfaces at the caller's next
+ * synchronisation and is undefined behaviour.
+ *
+ * Errors.  Every entry point returns ATTN_OK or one of the codes below and
+ * never aborts; no C++ exception crosses the ABI.  Arguments are validated on
+ * the host before anything is launched; on an error nothing is launched and
+ * attn_last_error() describes the first problem found.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* element types of q, k, v, o and the KV cache */
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
+
+/* status codes */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is negative / inconsistent (h_q % h_kv != 0, ...) */
+  ATTN_ERR_UNSUPPORTED = 3, /* a valid but unsupported dtype / head_dim / block size / group */
+  ATTN_ERR_WORKSPACE = 4,   /* decode workspace missing or smaller than required */
+  ATTN_ERR_ALIGN = 5,       /* a base pointer or row stride is not 16-byte aligned */
+  ATTN_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+};
+
+/* ABI version of the loaded library (ATTN_ABI_VERSION). */
+int attn_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* attn_last_error(void);
+
+/*
+ * attn_fwd -- prefill: O = softmax(Q K^T * softmax_scale [+ causal mask]) V.
+ *
+ *   dtype          ATTN_F32, ATTN_F16 or ATTN_BF16 (q, k, v and o share it).
+ *   q              [batch][n_q][h_q][head_dim] addressed by q_stride.
+ *   k, v           [batch][n_k][h_kv][head_dim] addressed by k_stride / v_stride.
+ *   o              [batch][n_q][h_q][head_dim] addressed by o_stride (written).
+ *   lse            optional [batch][h_q][n_q] fp32, contiguous, natural-log
+ *                  log-sum-exp of each row's visible logits (written); NULL
+ *                  to skip.
+ *   x_stride[3]    element strides of the (batch, sequence, head) dimensions;
+ *                  the head_dim stride is 1.  Host arrays.
+ *   head_dim       64 or 128.
+ *   h_q, h_kv      h_q % h_kv == 0.
+ *   softmax_scale  finite and > 0 (1/sqrt(head_dim) in the usual case).
+ *   causal         0 or 1 (bottom-right aligned mask, see above).
+ *   stream         hipStream_t or NULL.
+ *
+ * Alignment: base pointers 16-byte aligned; every sequence and head stride
+ * (and batch stride) times the element size a multiple of 16 bytes.
+ * batch, n_q or h_q equal to 0 is a no-op; n_k == 0 writes o = 0 and
+ * lse = -inf.  Host-side errors only: ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED,
+ * _ALIGN; ATTN_ERR_HIP if the launch fails.
+ */
+int attn_fwd(int dtype,
+             const void* q, const void* k, const void* v, void* o, float* lse,
+             int batch, int n_q, int n_k, int h_q, int h_kv, int head_dim,
+             const int64_t* q_stride, const int64_t* k_stride,
+             const int64_t* v_stride, const int64_t* o_stride,
+             float softmax_scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace paged_attn_decode needs for these sizes (the
+ * split-K partial results).  Returns 0 for non-positive sizes.
+ */
+size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int head_dim,
+                                        int max_context_len);
+
+/*
+ * paged_attn_decode -- one query token per sequence attending to its whole
+ * cached context through a block table.
+ *
+ *   dtype               ATTN_F16 or ATTN_BF16.
+ *   q                   [num_seqs][h_q][head_dim], contiguous.
+ *   k_cache, v_cache    [num_blocks][h_kv][block_size][head_dim] each,
+ *                       contiguous.  Logical token t of sequence s lives at
+ *                       block block_table[s][t / block_size], slot
+ *                       t % block_size.  The same block id may appear in
+ *                       several rows (shared prefixes); blocks are only read.
+ *   block_table         device [num_seqs][max_blocks_per_seq] int32; only the
+ *                       first ceil(context_lens[s] / block_size) entries of a
+ *                       row are read, and each must be in [0, num_blocks).
+ *   context_lens        device [num_seqs] int32, each in [0, max_context_len];
+ *                       the query attends to all context_lens[s] tokens (the
+ *                       length includes the current token).  0 gives o = 0
+ *                       and lse = -inf.
+ *   o                   [num_seqs][h_q][head_dim], contiguous (written).
+ *   lse                 optional [num_seqs][h_q] fp32 (written); NULL to skip.
+ *   head_dim            64 or 128.   block_size: 16.
+ *   h_q / h_kv          a group of at most 16 query heads per KV head.
+ *   max_context_len     upper bound of context_lens, host-side; fixes the
+ *                       grid and the workspace size.
+ *   max_blocks_per_seq  >= ceil(max_context_len / block_size).
+ *   workspace           device memory of at least
+ *                       paged_attn_decode_workspace_size(num_seqs, h_q,
+ *                       head_dim, max_context_len) bytes, 16-byte aligned,
+ *                       owned by the caller; its contents on entry do not
+ *                       matter and are garbage on exit.
+ *   stream              hipStream_t or NULL.
+ *
+ * Two kernels are enqueued: a split kernel over (sequence, KV head, context
+ * partition) and a combine kernel that merges the partitions' partial
+ * results by their log-sum-exp.  Results do not depend on which physical
+ * blocks hold the data: the same logical sequence gives bit-identical
+ * outputs under any block table.  num_seqs == 0 is a no-op.
+ */
+int paged_attn_decode(int dtype,
+                      const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* context_lens,
+                      void* o, float* lse,
+                      int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                      int max_blocks_per_seq, int max_context_len, int num_blocks,
+                      float softmax_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

@@ -201,10 +201,9 @@ def gather_paged_kv(pool, table_row, context_len, block_size):
     ``pool[table_row[t // block_size], :, t % block_size, :]``.  Returns
     ``[context_len][Hkv][d]``.
     """
-    pool = _f64(pool)
     t = np.arange(int(context_len))
     phys = np.asarray(table_row, dtype=np.int64)[t // block_size]
-    return pool[phys, :, t % block_size, :]
+    return _f64(np.asarray(pool)[phys, :, t % block_size, :])
 
 
 def paged_decode(q, k_pool, v_pool, block_table, context_lens, block_size, scale=None):

@@ -1,0 +1,69 @@
+"""Comparison gates shared by the GPU parity tests.
+
+Tolerances (from the subject's acceptance bar):
+  * fp32 outputs: max-abs error <= 1e-5 against the fp64 oracle;
+  * bf16 / fp16 outputs: mean-abs error <= 1e-3, and max-abs error <= 1e-2
+    measured beyond half an output ulp.  A 16-bit output cannot be closer to
+    the exact value than half an ulp of its own format: for bf16 and
+    |O| >= 4 that is 2^-6 = 0.0156 > 1e-2, so even the exactly rounded result
+    would fail a raw 1e-2 bound on the rare large outputs of the stress
+    workload.  The gate therefore charges max(0, |gpu - ref| - ulp/2); the raw
+    max-abs error and the number of raw exceedances are reported as well.
+No NaN or Inf is allowed anywhere.
+"""
+
+import numpy as np
+import torch
+
+MANT_BITS = {torch.bfloat16: 7, torch.float16: 10, torch.float32: 23}
+
+
+def half_ulp(ref, dtype):
+    """Half an ulp of ``dtype`` at each |ref| (normal range)."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return np.ldexp(1.0, (e - MANT_BITS[dtype] - 1).astype(np.int64))
+
+
+def compare(gpu, ref, dtype):
+    """Error report of a GPU output (tensor) against the fp64 oracle (ndarray)."""
+    g = gpu.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(gpu) else gpu
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    finite = bool(np.all(np.isfinite(g)))
+    err = np.abs(g - ref)
+    rep = {
+        "finite": finite,
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "mean_abs": float(err.mean()) if err.size else 0.0,
+        "raw_exceed_1e-2": int((err > 1e-2).sum()),
+    }
+    if dtype == torch.float32:
+        rep["gated_max"] = rep["max_abs"]
+    else:
+        rep["gated_max"] = float(np.max(np.maximum(0.0, err - half_ulp(ref, dtype)), initial=0.0))
+    return rep
+
+
+def assert_close(gpu, ref, dtype, what=""):
+    rep = compare(gpu, ref, dtype)
+    print("%s %s" % (what, rep), flush=True)
+    assert rep["finite"], "%s: non-finite output" % what
+    if dtype == torch.float32:
+        assert rep["max_abs"] <= 1e-5, "%s: %s" % (what, rep)
+    else:
+        assert rep["mean_abs"] <= 1e-3, "%s: %s" % (what, rep)
+        assert rep["gated_max"] <= 1e-2, "%s: %s" % (what, rep)
+    return rep
+
+
+def assert_lse_close(gpu_lse, ref_lse, tol=1e-3, what=""):
+    g = gpu_lse.detach().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref_lse, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(g)), "%s: lse finiteness differs" % what
+    assert np.all(g[~fin] == -np.inf)
+    if fin.any():
+        err = np.abs(g[fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))
+        print("%s lse rel-max %.3e" % (what, err.max()), flush=True)
+        assert err.max() <= tol, "%s: lse error %.3e" % (what, err.max())

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/attn.h declares, and rejects invalid arguments on the host before any
+device work (these calls never reach a launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_34_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "paged_attn_decode", "paged_attn_decode_workspace_size",
+              "attn_last_error", "attn_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ea.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert ea.abi_version() == 1
+
+
+def test_workspace_size():
+    # one partition (<= 512 tokens) needs no workspace
+    assert ea.paged_attn_decode_workspace_size(64, 32, 128, 512) == 0
+    assert ea.paged_attn_decode_workspace_size(0, 32, 128, 8192) == 0
+    # 16 partitions of 512: 64 * 32 * 16 slots of (128 + 2) floats
+    assert ea.paged_attn_decode_workspace_size(64, 32, 128, 8192) == 64 * 32 * 16 * 130 * 4
+    assert ea.paged_attn_decode_workspace_size(2, 4, 64, 513) == 2 * 4 * 2 * 66 * 4
+
+
+FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
+I64x3 = ctypes.c_int64 * 3
+
+
+def _fwd(dtype=2, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, batch=1, n_q=128, n_k=128, h_q=4,
+         h_kv=2, d=128, qs=(128 * 4 * 128, 4 * 128, 128), ks=(128 * 2 * 128, 2 * 128, 128),
+         scale=0.088, causal=0, strides=True):
+    L = ea.lib()
+    st = [I64x3(*qs), I64x3(*ks), I64x3(*ks), I64x3(*qs)] if strides else [None] * 4
+    code = L.attn_fwd(dtype, q, k, v, o, lse, batch, n_q, n_k, h_q, h_kv, d, *st, scale, causal,
+                      None)
+    return code, L.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 3),
+    (dict(d=96), 3),
+    (dict(h_q=3, h_kv=2), 2),
+    (dict(h_kv=0), 2),
+    (dict(n_q=-1), 2),
+    (dict(scale=float("nan")), 2),
+    (dict(scale=0.0), 2),
+    (dict(causal=2), 2),
+    (dict(q=None), 1),
+    (dict(k=None), 1),
+    (dict(strides=False), 1),
+    (dict(q=FAKE + 8), 5),
+    (dict(qs=(128 * 4 * 128, 4 * 128, 4)), 5),    # head stride of 8 bytes
+    (dict(lse=FAKE + 2), 5),
+])
+def test_attn_fwd_rejects(kw, code):
+    got, msg = _fwd(**kw)
+    assert got == code, msg
+    assert msg.startswith("attn_fwd")
+
+
+def test_attn_fwd_empty_problem_is_noop():
+    # nothing to compute: returns OK without touching any pointer
+    assert _fwd(batch=0, q=None, o=None)[0] == 0
+    assert _fwd(n_q=0, q=None, o=None)[0] == 0
+
+
+def _dec(dtype=2, q=FAKE, k=FAKE, v=FAKE, table=FAKE, ctx=FAKE, o=FAKE, lse=None, S=4, h_q=32,
+         h_kv=8, d=128, bs=16, mbps=512, mcl=8192, nb=100, scale=0.088, ws=FAKE, ws_bytes=None):
+    L = ea.lib()
+    if ws_bytes is None:
+        ws_bytes = L.paged_attn_decode_workspace_size(S, h_q, d, mcl)
+    code = L.paged_attn_decode(dtype, q, k, v, table, ctx, o, lse, S, h_q, h_kv, d, bs, mbps, mcl,
+                               nb, scale, ws, ws_bytes, None)
+    return code, L.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 3),
+    (dict(d=80), 3),
+    (dict(bs=32), 3),
+    (dict(h_q=64, h_kv=2), 3),       # group of 32
+    (dict(h_q=30), 2),
+    (dict(mbps=100), 2),             # 100 * 16 < 8192
+    (dict(nb=0), 2),
+    (dict(scale=-1.0), 2),
+    (dict(q=None), 1),
+    (dict(table=None), 1),
+    (dict(ctx=None), 1),
+    (dict(ws=None), 4),
+    (dict(ws_bytes=100), 4),
+    (dict(k=FAKE + 4), 5),
+    (dict(ws=FAKE + 8), 5),
+    (dict(table=FAKE + 2), 5),
+])
+def test_paged_decode_rejects(kw, code):
+    got, msg = _dec(**kw)
+    assert got == code, msg
+    assert msg.startswith("paged_attn_decode")
+
+
+def test_paged_decode_no_sequences_is_noop():
+    assert _dec(S=0, q=None, o=None, ctx=None)[0] == 0
+
+
+def test_last_error_cleared_on_success():
+    _fwd(dtype=7)
+    assert ea.lib().attn_last_error().decode() != ""
+    assert _fwd(batch=0)[0] == 0
+    assert ea.lib().attn_last_error().decode() == ""
