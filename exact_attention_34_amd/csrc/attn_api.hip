@@ -1,5 +1,6 @@
 // C ABI of libattn.so (declared in include/attn.h): host-side validation and
 // dispatch.  Nothing here allocates device memory or synchronises.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -82,6 +83,13 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
         if ((st[i] * es) % 16 != 0)
           return fail(ATTN_ERR_ALIGN, "attn_fwd: batch/sequence/head strides must be multiples of 16 bytes");
       }
+
+    if (n_k > 1 && (k_stride[1] < head_dim || v_stride[1] < head_dim))
+      return fail(ATTN_ERR_SHAPE, "attn_fwd: k and v sequence strides must be >= head_dim");
+    // K/V tiles are addressed with 32-bit byte offsets within one
+    // (batch, kv head) slice, including up to one tile past its end
+    if (((int64_t)n_k + 128) * std::max(k_stride[1], v_stride[1]) * es >= ((int64_t)1 << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: one (batch, kv head) slice of k/v spans >= 2 GiB");
 
     attn::FwdParams p{};
     p.q = q;

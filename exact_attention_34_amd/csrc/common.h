@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -38,6 +39,11 @@ struct BF16 {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
+  // acc + (both packed values): the fp32 sum of the rounded probabilities
+  __device__ static inline float sum2(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
   // widen the low / high 16-bit half of a dword to fp32 (exact)
   __device__ static inline float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
   __device__ static inline float hi(uint32_t w) {
@@ -59,6 +65,10 @@ struct F16 {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
+  __device__ static inline float sum2(uint32_t w, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+  }
   __device__ static inline float lo(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
   }
@@ -78,8 +88,31 @@ __device__ inline uint32_t join_hi16(uint32_t a, uint32_t b) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value held by lane (l xor 32).
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
+// max / sum of a value over the lane pair (l, l xor 32): v_permlane32_swap of
+// x with itself leaves {x[l % 32], x[l % 32 + 32]} in the two results.
+__device__ inline float pair_max32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ inline float pair_sum32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Raw buffer resource over [base, base + bytes): loads whose byte offset
+// (the VGPR offset) is at or past `bytes` return zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 
 struct FwdParams {
   const void* q;
@@ -92,6 +125,7 @@ struct FwdParams {
   int64_t vs_b, vs_n, vs_h;
   int64_t os_b, os_n, os_h;
   int batch, n_q, n_k, h_q, h_kv, group;
+  uint32_t k_bytes, v_bytes;  // byte extent of one (batch, kv head) slice of k / v
   int n_qtiles;     // ceil(n_q / BM)
   int num_items;    // n_qtiles * batch * h_q
   int xcd_chunk;    // work items kept together on one XCD (0 = no remap)

@@ -55,16 +55,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void attn_fwd_mfma_kernel(FwdParams p) {
   typedef typename TT::elem T;
   constexpr int BM = 128, BN = 64;
-  constexpr int KLD = D + 8;   // LDS row stride of K, elements (16 B pad)
-  constexpr int VLD = BN + 8;  // LDS row stride of V^T, elements (16 B pad)
+  constexpr int KLD = D + 8;    // LDS row pitch of K tiles, elements (272 B for d = 128)
+  constexpr int VLD = D + 16;   // LDS row pitch of V tiles, elements (288 B for d = 128)
   constexpr int KSZ = BN * KLD;
-  constexpr int VSZ = D * VLD;
-  constexpr int STAGE = KSZ + VSZ;
-  constexpr int KCH = BN * D / 8 / 256;   // 16-byte K chunks per thread
-  constexpr int VUNITS = (BN / 8) * (D / 4);  // (8 keys x 4 d) V units
-  static_assert(KCH * 256 * 8 == BN * D, "K tile split");
-  static_assert(VUNITS <= 256, "V tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  constexpr int VSZ = BN * VLD;
+  constexpr int CH = BN * D / 8 / 256;   // 16-byte chunks of K (and of V) per thread
+  // The running max is only raised when a row's maximum exceeds it by more
+  // than TAU (log2 units); until then probabilities are taken relative to the
+  // stale max and stay below 2^TAU.  The final division by l uses the same
+  // reference, so the result is unchanged; the O rescale is skipped whenever
+  // no row of the wave moved.
+  constexpr float TAU = 8.0f;
+  static_assert(CH * 256 * 8 == BN * D, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * KSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * VSZ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -92,6 +96,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const T* Kg = (const T*)p.k + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
+  const uint32_t krow = (uint32_t)p.ks_n * 2u, vrow = (uint32_t)p.vs_n * 2u;  // row pitch, bytes
 
   // Q fragment (B operand of S^T = K Q^T): column = query, k = d.
   const int qrow = q0 + wave * 32 + col;
@@ -107,143 +112,168 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-  float m_run = -INFINITY;  // running max, log2 units (same in lanes l, l^32)
+  float m_run = -INFINITY;  // reference max, log2 units (same in lanes l, l^32)
   float l_run = 0.f;        // running sum over this lane's keys
+  const float c = p.scale_log2;
 
-  // ---- global -> register staging of one K/V tile ----
-  u32x4 kreg[KCH];
-  u32x2 vreg[8];
-  // V unit of this thread: 8 keys x 4 consecutive d.  Within each group of
-  // 16 keys the LDS position order is keys 0-3, 8-11, 4-7, 12-15, which is
-  // the order in which the score registers of a lane feed the P^T operand.
-  const int vdq = tid % (D / 4);
-  const int vko = tid / (D / 4);
-  const int vkey_base = (vko >> 1) * 16 + (vko & 1) * 4;
-
-  auto gload = [&](int kt) {
-    const int k0 = kt * BN;
+  // ---- tile staging: HBM -> registers -> LDS, both tiles row-major ----
+  uint32_t koff[CH], voff[CH];
+  int kdst[CH], vdst[CH];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      const int key = k0 + row;
-      kreg[c] = u32x4{0, 0, 0, 0};
-      if (key < p.n_k) kreg[c] = *(const u32x4*)(Kg + (int64_t)key * p.ks_n + ch * 8);
-    }
-    if (tid < VUNITS) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = k0 + vkey_base + (j & 3) + (j >> 2) * 8;
-        vreg[j] = u32x2{0, 0};
-        if (key < p.n_k) vreg[j] = *(const u32x2*)(Vg + (int64_t)key * p.vs_n + vdq * 4);
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint16_t* Ks = smem + stage * STAGE;
-    uint16_t* Vs = Ks + KSZ;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      *(u32x4*)(Ks + row * KLD + ch * 8) = kreg[c];
-    }
-    if (tid < VUNITS) {
-      // transpose 8 keys x 4 d into 4 rows (one per d) of 8 keys
-      u32x4 w0, w1, w2, w3;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 a = vreg[2 * w], c2 = vreg[2 * w + 1];
-        w0[w] = join_lo16(a.x, c2.x);
-        w1[w] = join_hi16(a.x, c2.x);
-        w2[w] = join_lo16(a.y, c2.y);
-        w3[w] = join_hi16(a.y, c2.y);
-      }
-      uint16_t* vrow = Vs + (vdq * 4) * VLD + vko * 8;
-      *(u32x4*)(vrow + 0 * VLD) = w0;
-      *(u32x4*)(vrow + 1 * VLD) = w1;
-      *(u32x4*)(vrow + 2 * VLD) = w2;
-      *(u32x4*)(vrow + 3 * VLD) = w3;
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
+  for (int cc = 0; cc < CH; ++cc) {
+    const int idx = tid + 256 * cc;
+    const int row = idx / (D / 8), ch = idx % (D / 8);
+    koff[cc] = (uint32_t)row * krow + ch * 16;
+    voff[cc] = (uint32_t)row * vrow + ch * 16;
+    kdst[cc] = row * KLD + ch * 8;
+    vdst[cc] = row * VLD + ch * 8;
   }
-  __syncthreads();
+  u32x4 kreg[CH], vreg[CH];
+  // Per-lane offsets stay fixed; each tile gets a buffer resource based at its
+  // first row (scalar arithmetic) whose extent is what is left of the slice,
+  // so rows past n_k load as zero.
+  auto gload_k = [&](int kt) {
+    const uint32_t o = (uint32_t)(kt * BN) * krow;
+    const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.k_bytes > o ? p.k_bytes - o : 0u);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Kg + o, rem_b);
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) kreg[cc] = buf_load16(r, koff[cc]);
+  };
+  auto gload_v = [&](int kt) {
+    const uint32_t o = (uint32_t)(kt * BN) * vrow;
+    const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.v_bytes > o ? p.v_bytes - o : 0u);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Vg + o, rem_b);
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) vreg[cc] = buf_load16(r, voff[cc]);
+  };
+  auto lstore_k = [&](int stage) {
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) *(u32x4*)(ks_lds + stage * KSZ + kdst[cc]) = kreg[cc];
+  };
+  auto lstore_v = [&](int stage) {
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) *(u32x4*)(vs_lds + stage * VSZ + vdst[cc]) = vreg[cc];
+  };
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
-    const uint16_t* Ks = smem + stage * STAGE;
-    const uint16_t* Vs = Ks + KSZ;
-
-    // ---- S^T = K Q^T for two 32-key sub-tiles ----
-    f32x16 st[2];
+  // ---- S^T = K Q^T for the two 32-key halves of a tile ----
+  auto qk = [&](int stage, f32x16 (&st)[2]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[sub][r] = 0.f;
-      const uint16_t* kp = Ks + (sub * 32 + col) * KLD + hi * 8;
+      const uint16_t* kp = ks_lds + stage * KSZ + (sub * 32 + col) * KLD + hi * 8;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) st[sub] = TT::mma32(*(const u32x4*)(kp + 16 * s), qf[s], st[sub]);
+      for (int s = 0; s < D / 16; ++s)
+        st[sub] = TT::mma32(*(const u32x4*)(kp + 16 * s), qf[s], st[sub]);
     }
+  };
 
-    // ---- scale, mask, online softmax ----
+  // V operand of O^T = V^T P^T through the transposing LDS read: within each
+  // group of 16 lanes, lane i receives element i % 4 of the 8-byte chunks
+  // loaded by lanes 4j + i/4 (j = 0..3).  Lane 4j + q of the group therefore
+  // points at key (slot base + j), d (group base + 4q), and every lane ends
+  // up with four keys of one d column.
+  const int vi = lane & 15, vg = lane >> 4;
+  const int v_lane_off = ((vg >> 1) * 4 + (vi >> 2)) * VLD + (vg & 1) * 16 + (vi & 3) * 4;
+
+  // last key visible to this lane's query, clamped to the sequence
+  const int klast = CAUSAL ? min(qrow + off, p.n_k - 1) : p.n_k - 1;
+
+  // ---- prologue: K_0, V_0 and K_1 staged; S_0 computed ----
+  if (ntiles > 0) {
+    gload_k(0);
+    gload_v(0);
+    lstore_k(0);
+    lstore_v(0);
+    if (ntiles > 1) gload_k(1);
+  }
+  __syncthreads();
+  f32x16 st_cur[2];
+  if (ntiles > 0) qk(0, st_cur);
+  if (ntiles > 1) lstore_k(1);
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    // prefetch: K of tile kt+2 and V of tile kt+1
+    if (kt + 2 < ntiles) gload_k(kt + 2);
+    if (kt + 1 < ntiles) gload_v(kt + 1);
+
+    // ---- S_{kt+1} on the matrix cores while the softmax of S_kt runs ----
+    f32x16 st_next[2];
+    if (kt + 1 < ntiles) qk((kt + 1) & 1, st_next);
+
     const int k0 = kt * BN;
     const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
-    float tmax = -INFINITY;
+    if (need_mask) {
+      // key of register r in half `sub`: k0 + hi*4 + sub*32 + (r/4)*8 + r%4
+      const int lim = klast - (k0 + hi * 4);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = sub * 32 + (r >> 2) * 8 + (r & 3);
+          st_cur[sub][r] = (rel <= lim) ? st_cur[sub][r] : -INFINITY;
+        }
+    }
+    float smax = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float t = st[sub][r] * p.scale_log2;
-        if (need_mask) {
-          const int key = k0 + sub * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          const bool vis = (key < p.n_k) && (!CAUSAL || key <= qrow + off);
-          t = vis ? t : -INFINITY;
-        }
-        st[sub][r] = t;
-        tmax = fmaxf(tmax, t);
-      }
-    tmax = fmaxf(tmax, xor32(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, st_cur[sub][r]);
+    const float tmax = pair_max32(smax) * c;
+    const bool grow = tmax > m_run + TAU;
+    // lanes that do not grow keep their reference (alpha = 1, which also
+    // covers rows that have not seen a visible key, m = -inf); a row leaving
+    // -inf gets alpha = 0
+    const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;
+    m_run = grow ? tmax : m_run;
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float psum = 0.f;
     u32x4 pb[4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(st[sub][r] - m_use);
-        const float p1 = fast_exp2(st[sub][r + 1] - m_use);
-        psum += p0 + p1;
-        pb[sub * 2 + (r >> 3)][(r & 7) >> 1] = TT::pack2(p0, p1);
+        const float p0 = fast_exp2(fmaf(st_cur[sub][r], c, neg_m));
+        const float p1 = fast_exp2(fmaf(st_cur[sub][r + 1], c, neg_m));
+        const uint32_t w = TT::pack2(p0, p1);
+        // l sums the rounded values that enter P V, so the normalisation
+        // matches the weights actually applied
+        psum = TT::sum2(w, psum);
+        pb[sub * 2 + (r >> 3)][(r & 7) >> 1] = w;
       }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T ----
+    const uint16_t* vb = vs_lds + (kt & 1) * VSZ + v_lane_off;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      for (int ks = 0; ks < BN / 16; ++ks) {
+        const uint16_t* a = vb + ks * 16 * VLD + t * 32;
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a)));
+        const u32x2 hi8 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a + 8 * VLD)));
+        oacc[t] = TT::mma32(u32x4{lo.x, lo.y, hi8.x, hi8.y}, pb[ks], oacc[t]);
+      }
 
-    // ---- O^T += V^T P^T ----
+    // ---- stage the prefetched tiles: K_{kt+2} over K_kt, V_{kt+1} over V_{kt-1} ----
+    if (kt + 2 < ntiles) lstore_k(kt & 1);
+    if (kt + 1 < ntiles) lstore_v((kt + 1) & 1);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      const uint16_t* vp = Vs + (t * 32 + col) * VLD + hi * 8;
-#pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks)
-        oacc[t] = TT::mma32(*(const u32x4*)(vp + ks * 16), pb[ks], oacc[t]);
-    }
-
-    if (kt + 1 < ntiles) lstore(stage ^ 1);
+    for (int sub = 0; sub < 2; ++sub) st_cur[sub] = st_next[sub];
     __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, LSE ----
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum32(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < p.n_q) {
     T* Og = (T*)p.o + (int64_t)b * p.os_b + (int64_t)qrow * p.os_n + (int64_t)h * p.os_h;
@@ -356,6 +386,9 @@ static hipError_t launch_mfma(FwdParams p, hipStream_t stream) {
   p.n_qtiles = (p.n_q + BM - 1) / BM;
   p.num_items = p.n_qtiles * p.batch * p.h_q;
   p.xcd_chunk = p.group > 1 ? p.group : 1;
+  // bytes from the first row of a (batch, kv head) slice to the end of its last row
+  p.k_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.ks_n + D) * 2) : 0u;
+  p.v_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.vs_n + D) * 2) : 0u;
   hipLaunchKernelGGL((attn_fwd_mfma_kernel<TT, D, CAUSAL>), dim3(p.num_items), dim3(256), 0,
                      stream, p);
   return hipGetLastError();

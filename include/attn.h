@@ -96,7 +96,10 @@ const char* attn_last_error(void);
  *   stream         hipStream_t or NULL.
  *
  * Alignment: base pointers 16-byte aligned; every sequence and head stride
- * (and batch stride) times the element size a multiple of 16 bytes.
+ * (and batch stride) times the element size a multiple of 16 bytes.  The
+ * sequence strides of k and v must be at least head_dim (rows do not
+ * overlap), and one (batch, kv head) slice of k or v must span less than
+ * 2 GiB.
  * batch, n_q or h_q equal to 0 is a no-op; n_k == 0 writes o = 0 and
  * lse = -inf.  Host-side errors only: ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED,
  * _ALIGN; ATTN_ERR_HIP if the launch fails.

@@ -57,13 +57,27 @@ def assert_close(gpu, ref, dtype, what=""):
     return rep
 
 
-def assert_lse_close(gpu_lse, ref_lse, tol=1e-3, what=""):
+# Log-sum-exp tolerance.  The kernels normalise by the sum of the
+# probabilities *as rounded* for the P V product (so that O's weights sum to
+# exactly what it is divided by); the log of that sum differs from the exact
+# log-sum-exp by at most ln(1 + 2^-(mantissa bits + 1)): 1.95e-3 for bf16,
+# 2.4e-4 for fp16.  fp32 inputs keep fp32 probabilities.  A relative term
+# covers the fp32 accumulation of the q.k dot product: its bound is about
+# d * 2^-24 = 7.6e-6 of sum_i |q_i k_i|, which for random rows exceeds |q.k|
+# by about sqrt(d) = 11, i.e. ~1e-4 of the logit (the stress rows reach
+# logits of ~1e3).
+LSE_TOL = {torch.bfloat16: 2.5e-3, torch.float16: 5e-4, torch.float32: 1e-5}
+
+
+def assert_lse_close(gpu_lse, ref_lse, dtype, what=""):
     g = gpu_lse.detach().cpu().numpy().astype(np.float64)
     ref = np.asarray(ref_lse, dtype=np.float64)
     fin = np.isfinite(ref)
     assert np.array_equal(fin, np.isfinite(g)), "%s: lse finiteness differs" % what
     assert np.all(g[~fin] == -np.inf)
     if fin.any():
-        err = np.abs(g[fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))
-        print("%s lse rel-max %.3e" % (what, err.max()), flush=True)
-        assert err.max() <= tol, "%s: lse error %.3e" % (what, err.max())
+        err = np.abs(g[fin] - ref[fin])
+        bound = LSE_TOL[dtype] + (1e-4 if dtype != torch.float32 else 1e-5) * np.abs(ref[fin])
+        print("%s lse max-abs %.3e (worst err/bound %.2f)" % (what, err.max(), (err / bound).max()),
+              flush=True)
+        assert np.all(err <= bound), "%s: lse error %.3e" % (what, err.max())

@@ -36,7 +36,7 @@ def _check(inp, what):
     out, lse = _run(inp)
     ref, ref_lse = _oracle(inp)
     assert_close(out, ref, TDT[inp.dtype], what)
-    assert_lse_close(lse, ref_lse, what=what)
+    assert_lse_close(lse, ref_lse, TDT[inp.dtype], what=what)
     return out, lse
 
 
@@ -104,7 +104,7 @@ def test_max_context_bound_above_actual():
     torch.cuda.synchronize()
     ref, ref_lse = _oracle(inp)
     assert_close(out, ref, torch.bfloat16, "max_context_len bound")
-    assert_lse_close(lse, ref_lse)
+    assert_lse_close(lse, ref_lse, torch.bfloat16)
 
 
 def test_decode_equals_last_row_of_causal_prefill():
