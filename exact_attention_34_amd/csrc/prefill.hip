@@ -50,25 +50,32 @@ __device__ inline int remap_item(int i, int num_items, int chunk) {
 // ----------------------------------------------------------------------------
 // 16-bit matrix-core kernel
 // ----------------------------------------------------------------------------
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 template <typename TT, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(FwdParams p) {
   typedef typename TT::elem T;
   constexpr int BM = 128, BN = 64;
-  constexpr int KLD = D + 8;    // LDS row pitch of K tiles, elements (272 B for d = 128)
-  constexpr int VLD = D + 16;   // LDS row pitch of V tiles, elements (288 B for d = 128)
-  constexpr int KSZ = BN * KLD;
-  constexpr int VSZ = BN * VLD;
-  constexpr int CH = BN * D / 8 / 256;   // 16-byte chunks of K (and of V) per thread
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int TILE = BN * D;            // elements per K or V tile (no padding)
+  constexpr int LOADS = BN * CPR / 256;   // 16-byte direct loads per thread per tile
+  constexpr int NS = D / 16;              // k-steps of one S^T half (8 for d = 128)
+  constexpr int NQK = 2 * NS;             // QK matrix ops per tile
+  constexpr int NPV = (D / 32) * (BN / 16);  // PV matrix ops per tile
   // The running max is only raised when a row's maximum exceeds it by more
   // than TAU (log2 units); until then probabilities are taken relative to the
   // stale max and stay below 2^TAU.  The final division by l uses the same
   // reference, so the result is unchanged; the O rescale is skipped whenever
   // no row of the wave moved.
   constexpr float TAU = 8.0f;
-  static_assert(CH * 256 * 8 == BN * D, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * KSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * VSZ];
+  static_assert(LOADS * 256 == BN * CPR, "tile split");
+  static_assert(32 % (NQK + NPV) == 0, "slot plan");
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -100,9 +107,9 @@ void attn_fwd_mfma_kernel(FwdParams p) {
 
   // Q fragment (B operand of S^T = K Q^T): column = query, k = d.
   const int qrow = q0 + wave * 32 + col;
-  u32x4 qf[D / 16];
+  u32x4 qf[NS];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
+  for (int s = 0; s < NS; ++s) {
     qf[s] = u32x4{0, 0, 0, 0};
     if (qrow < p.n_q) qf[s] = *(const u32x4*)(Qg + (int64_t)qrow * p.qs_n + 16 * s + hi * 8);
   }
@@ -116,160 +123,251 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   float l_run = 0.f;        // running sum over this lane's keys
   const float c = p.scale_log2;
 
-  // ---- tile staging: HBM -> registers -> LDS, both tiles row-major ----
-  uint32_t koff[CH], voff[CH];
-  int kdst[CH], vdst[CH];
+  // ---- tiles go HBM -> LDS directly (no registers) ----
+  // LDS tile layout: row-major, 16-byte chunks permuted within each row so
+  // that the column-wise operand reads hit distinct banks:
+  //   K: chunk c of row r sits at c ^ (r % 16)   (16 rows x 1 chunk per read)
+  //   V: chunk c of row r sits at c ^ 4 (r % 4)  (4 rows x 4 chunks per read
+  //                                                of 32 lanes)
+  // A direct load writes 64 consecutive 16-byte LDS slots per wave
+  // instruction, so every lane fetches the global chunk that belongs in its
+  // slot.
+  auto kswz = [](int r) { return (r & 15) & (CPR - 1); };
+  auto vswz = [](int r) { return (4 * (r & 3)) & (CPR - 1); };
+  uint32_t kgo[LOADS], vgo[LOADS];
 #pragma unroll
-  for (int cc = 0; cc < CH; ++cc) {
-    const int idx = tid + 256 * cc;
-    const int row = idx / (D / 8), ch = idx % (D / 8);
-    koff[cc] = (uint32_t)row * krow + ch * 16;
-    voff[cc] = (uint32_t)row * vrow + ch * 16;
-    kdst[cc] = row * KLD + ch * 8;
-    vdst[cc] = row * VLD + ch * 8;
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    kgo[i] = (uint32_t)row * krow + (uint32_t)((pc ^ kswz(row)) * 16);
+    vgo[i] = (uint32_t)row * vrow + (uint32_t)((pc ^ vswz(row)) * 16);
   }
-  u32x4 kreg[CH], vreg[CH];
   // Per-lane offsets stay fixed; each tile gets a buffer resource based at its
   // first row (scalar arithmetic) whose extent is what is left of the slice,
   // so rows past n_k load as zero.
-  auto gload_k = [&](int kt) {
+  auto load_k = [&](int kt, int stage) {
     const uint32_t o = (uint32_t)(kt * BN) * krow;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.k_bytes > o ? p.k_bytes - o : 0u);
     const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Kg + o, rem_b);
 #pragma unroll
-    for (int cc = 0; cc < CH; ++cc) kreg[cc] = buf_load16(r, koff[cc]);
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
   };
-  auto gload_v = [&](int kt) {
+  auto load_v = [&](int kt, int stage) {
     const uint32_t o = (uint32_t)(kt * BN) * vrow;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.v_bytes > o ? p.v_bytes - o : 0u);
     const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Vg + o, rem_b);
 #pragma unroll
-    for (int cc = 0; cc < CH; ++cc) vreg[cc] = buf_load16(r, voff[cc]);
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, vs_lds + stage * TILE + (i * 4 + wave) * 512, vgo[i]);
   };
-  auto lstore_k = [&](int stage) {
-#pragma unroll
-    for (int cc = 0; cc < CH; ++cc) *(u32x4*)(ks_lds + stage * KSZ + kdst[cc]) = kreg[cc];
-  };
-  auto lstore_v = [&](int stage) {
-#pragma unroll
-    for (int cc = 0; cc < CH; ++cc) *(u32x4*)(vs_lds + stage * VSZ + vdst[cc]) = vreg[cc];
+  // Direct loads complete into LDS asynchronously: wait for them, then
+  // barrier, before any wave reads the stage.
+  auto wait_loads_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
-  // ---- S^T = K Q^T for the two 32-key halves of a tile ----
-  auto qk = [&](int stage, f32x16 (&st)[2]) {
+  // ---- LDS read addresses, fixed per lane (elements) ----
+  // K operand of S^T = K Q^T, k-step s: row col (+32 for the second half),
+  // logical chunk 2s + hi.
+  int kofs[NS];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[sub][r] = 0.f;
-      const uint16_t* kp = ks_lds + stage * KSZ + (sub * 32 + col) * KLD + hi * 8;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        st[sub] = TT::mma32(*(const u32x4*)(kp + 16 * s), qf[s], st[sub]);
-    }
-  };
-
+  for (int s = 0; s < NS; ++s) kofs[s] = col * D + (((2 * s + hi) ^ kswz(col)) * 8);
   // V operand of O^T = V^T P^T through the transposing LDS read: within each
-  // group of 16 lanes, lane i receives element i % 4 of the 8-byte chunks
+  // group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces
   // loaded by lanes 4j + i/4 (j = 0..3).  Lane 4j + q of the group therefore
-  // points at key (slot base + j), d (group base + 4q), and every lane ends
-  // up with four keys of one d column.
+  // points at key (slot base + j) and d (group base + 4q); every lane ends up
+  // with four keys of one d column.  Keys of the second read are 8 further;
+  // k-steps add 16 rows.  (Row offsets that are multiples of 4 leave the
+  // swizzle unchanged, so they fold into immediates.)
   const int vi = lane & 15, vg = lane >> 4;
-  const int v_lane_off = ((vg >> 1) * 4 + (vi >> 2)) * VLD + (vg & 1) * 16 + (vi & 3) * 4;
+  const int v_row0 = (vg >> 1) * 4 + (vi >> 2);
+  int vofs[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int el = t * 32 + (vg & 1) * 16 + (vi & 3) * 4;
+    vofs[t] = v_row0 * D + ((((el >> 3) ^ vswz(v_row0)) * 8) + (el & 7));
+  }
 
   // last key visible to this lane's query, clamped to the sequence
   const int klast = CAUSAL ? min(qrow + off, p.n_k - 1) : p.n_k - 1;
 
-  // ---- prologue: K_0, V_0 and K_1 staged; S_0 computed ----
   if (ntiles > 0) {
-    gload_k(0);
-    gload_v(0);
-    lstore_k(0);
-    lstore_v(0);
-    if (ntiles > 1) gload_k(1);
-  }
-  __syncthreads();
-  f32x16 st_cur[2];
-  if (ntiles > 0) qk(0, st_cur);
-  if (ntiles > 1) lstore_k(1);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // prefetch: K of tile kt+2 and V of tile kt+1
-    if (kt + 2 < ntiles) gload_k(kt + 2);
-    if (kt + 1 < ntiles) gload_v(kt + 1);
-
-    // ---- S_{kt+1} on the matrix cores while the softmax of S_kt runs ----
-    f32x16 st_next[2];
-    if (kt + 1 < ntiles) qk((kt + 1) & 1, st_next);
-
-    const int k0 = kt * BN;
-    const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
-    if (need_mask) {
-      // key of register r in half `sub`: k0 + hi*4 + sub*32 + (r/4)*8 + r%4
-      const int lim = klast - (k0 + hi * 4);
+    // ---- prologue: K_0 and K_1 staged, the "previous" V stage zeroed, S_0 ----
+    load_k(0, 0);
+    load_k(1, 1);
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+    for (int i = 0; i < TILE / 8 / 256; ++i)
+      *(u32x4*)(vs_lds + TILE + (tid + 256 * i) * 8) = u32x4{0, 0, 0, 0};
+    wait_loads_and_sync();
+    f32x16 st_cur[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = sub * 32 + (r >> 2) * 8 + (r & 3);
-          st_cur[sub][r] = (rel <= lim) ? st_cur[sub][r] : -INFINITY;
-        }
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st_cur[sub][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        st_cur[sub] = TT::mma32(*(const u32x4*)(ks_lds + sub * 32 * D + kofs[s]), qf[s], st_cur[sub]);
     }
-    float smax = -INFINITY;
+    float smax_cur = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, st_cur[sub][r]);
-    const float tmax = pair_max32(smax) * c;
-    const bool grow = tmax > m_run + TAU;
-    // lanes that do not grow keep their reference (alpha = 1, which also
-    // covers rows that have not seen a visible key, m = -inf); a row leaving
-    // -inf gets alpha = 0
-    const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;
-    m_run = grow ? tmax : m_run;
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    float psum = 0.f;
-    u32x4 pb[4];
+      for (int r = 0; r < 16; ++r) smax_cur = fmaxf(smax_cur, st_cur[sub][r]);
+    u32x4 pb_prev[4];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int i = 0; i < 4; ++i) pb_prev[i] = u32x4{0, 0, 0, 0};
+    float pend_alpha = 1.f;
+    bool pend_grow = false;
+    __syncthreads();   // every wave is done with K stage 0 before it is refilled
+
+    // One tile.  Reads stage S (K_{kt+1}, V_{kt-1}); loads go to stage S ^ 1.
+    auto tile = [&](const int kt, auto SC) {
+      constexpr int S = decltype(SC)::value;
+      // all waves are done with the stage refilled below, and the tiles
+      // loaded last time have landed
+      if (kt > 0) wait_loads_and_sync();
+      // K_{kt+2} replaces K_kt (read for S_kt last tile); V_kt replaces
+      // V_{kt-2} (read for its P V last tile)
+      load_k(kt + 2, S ^ 1);
+      load_v(kt, S ^ 1);
+      // O holds P_{kt-2} V_{kt-2}: move it to the reference of tile kt-1
+      if (pend_grow) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(st_cur[sub][r], c, neg_m));
-        const float p1 = fast_exp2(fmaf(st_cur[sub][r + 1], c, neg_m));
-        const uint32_t w = TT::pack2(p0, p1);
-        // l sums the rounded values that enter P V, so the normalisation
-        // matches the weights actually applied
-        psum = TT::sum2(w, psum);
-        pb[sub * 2 + (r >> 3)][(r & 7) >> 1] = w;
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
       }
-    l_run = l_run * alpha + psum;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const int k0 = kt * BN;
+      const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
+      if (need_mask) {
+        // key of register r in half `sub`: k0 + hi*4 + sub*32 + (r/4)*8 + r%4
+        const int lim = klast - (k0 + hi * 4);
+        smax_cur = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-    }
+          for (int r = 0; r < 16; ++r) {
+            const int rel = sub * 32 + (r >> 2) * 8 + (r & 3);
+            st_cur[sub][r] = (rel <= lim) ? st_cur[sub][r] : -INFINITY;
+            smax_cur = fmaxf(smax_cur, st_cur[sub][r]);
+          }
+      }
+      const float tmax = pair_max32(smax_cur) * c;
+      const bool grow = tmax > m_run + TAU;
+      // lanes that do not grow keep their reference (alpha = 1, which also
+      // covers rows that have not seen a visible key, m = -inf); a row
+      // leaving -inf gets alpha = 0
+      const float alpha = fast_exp2(grow ? m_run - tmax : 0.f);
+      m_run = grow ? tmax : m_run;
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
-    // ---- O^T += V^T P^T ----
-    const uint16_t* vb = vs_lds + (kt & 1) * VSZ + v_lane_off;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        const uint16_t* a = vb + ks * 16 * VLD + t * 32;
+      // ---- 32 slots: one matrix op each (S_{kt+1} then O += P_{kt-1}
+      // V_{kt-1}), its LDS operand fetched two slots ahead, and a few vector
+      // ops of the softmax of S_kt / the row max of S_{kt+1} ----
+      const uint16_t* kb = ks_lds + S * TILE;
+      const uint16_t* vb = vs_lds + S * TILE;
+      auto fetch = [&](int i) -> u32x4 {
+        if (i < NQK) return *(const u32x4*)(kb + (i / NS) * 32 * D + kofs[i % NS]);
+        const int j = i - NQK, t = j / (BN / 16), ks = j % (BN / 16);
+        const uint16_t* a = vb + ks * 16 * D + vofs[t];
         const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(a)));
         const u32x2 hi8 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(a + 8 * VLD)));
-        oacc[t] = TT::mma32(u32x4{lo.x, lo.y, hi8.x, hi8.y}, pb[ks], oacc[t]);
-      }
-
-    // ---- stage the prefetched tiles: K_{kt+2} over K_kt, V_{kt+1} over V_{kt-1} ----
-    if (kt + 2 < ntiles) lstore_k(kt & 1);
-    if (kt + 1 < ntiles) lstore_v((kt + 1) & 1);
+            (__attribute__((address_space(3))) i16x4*)(a + 8 * D)));
+        return u32x4{lo.x, lo.y, hi8.x, hi8.y};
+      };
+      constexpr int NSLOT = NQK + NPV;
+      f32x16 st_next[2];
+      u32x4 pb_cur[4];
+      float psum = 0.f, pe_prev = 0.f, smax_next = -INFINITY;
+      u32x4 opnd[NSLOT];
+      opnd[0] = fetch(0);
+      opnd[1] = fetch(1);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) st_cur[sub] = st_next[sub];
-    __syncthreads();
+      for (int i = 0; i < NSLOT; ++i) {
+        if (i + 2 < NSLOT) opnd[i + 2] = fetch(i + 2);
+        if (i < NQK) {
+          const int sub = i / NS, s = i % NS;
+          if (s == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st_next[sub][r] = 0.f;
+          }
+          st_next[sub] = TT::mma32(opnd[i], qf[s], st_next[sub]);
+        } else {
+          const int j = i - NQK, t = j / (BN / 16), ks = j % (BN / 16);
+          oacc[t] = TT::mma32(opnd[i], pb_prev[ks], oacc[t]);
+        }
+        // softmax of S_kt: 32 probabilities per lane spread over the slots,
+        // packed in pairs
+#pragma unroll
+        for (int e = i * 32 / NSLOT; e < (i + 1) * 32 / NSLOT; ++e) {
+          const int sub = e / 16, r = e % 16;
+          // the empty volatile statements keep this slot's vector work
+          // between this slot's neighbours in the instruction stream
+          float x = st_cur[sub][r];
+          asm volatile("" : "+v"(x));
+          float pe = fast_exp2(fmaf(x, c, neg_m));
+          asm volatile("" : "+v"(pe));
+          if (r & 1) {
+            const uint32_t w = TT::pack2(pe_prev, pe);
+            // l sums the rounded values that enter P V, so the normalisation
+            // matches the weights actually applied
+            psum = TT::sum2(w, psum);
+            pb_cur[sub * 2 + (r >> 3)][(r & 7) >> 1] = w;
+          }
+          pe_prev = pe;
+        }
+        // row max of S_{kt+1}, once its products have landed
+        if (i >= NQK) {
+          const int j = i - NQK;                 // 0..NPV-1
+          const int e0 = j * 32 / NPV, e1 = (j + 1) * 32 / NPV;
+#pragma unroll
+          for (int e = e0; e < e1; ++e) smax_next = fmaxf(smax_next, st_next[e / 16][e % 16]);
+          asm volatile("" : "+v"(smax_next));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run = l_run * alpha + psum;
+      pend_alpha = alpha;
+      pend_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb_prev[i] = pb_cur[i];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) st_cur[sub] = st_next[sub];
+      smax_cur = smax_next;
+    };
+
+    int kt = 0;
+    for (; kt + 1 < ntiles; kt += 2) {
+      tile(kt, IntC<1>());
+      tile(kt + 1, IntC<0>());
+    }
+    if (kt < ntiles) {
+      tile(kt, IntC<1>());
+      ++kt;
+    }
+    wait_loads_and_sync();
+    // ---- the last P V (stage of tile ntiles - 1) ----
+    if (pend_grow) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
+    }
+    {
+      const uint16_t* vb = vs_lds + ((ntiles - 1) & 1) * TILE;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks) {
+          const uint16_t* a = vb + ks * 16 * D + vofs[t];
+          const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a)));
+          const u32x2 hi8 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a + 8 * D)));
+          oacc[t] = TT::mma32(u32x4{lo.x, lo.y, hi8.x, hi8.y}, pb_prev[ks], oacc[t]);
+        }
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE ----
