@@ -36,24 +36,26 @@ namespace attn {
 
 constexpr int kDecBS = 16;     // tokens per KV block
 constexpr int kDecPart = 512;  // tokens per partition
-constexpr int kDecWaves = 4;
 
-template <typename TT, int D, int GP>
-__global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeParams p) {
+template <typename TT, int D, int GP, int RING>
+__global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) {
   typedef typename TT::elem T;
   constexpr int NB = kDecPart / kDecBS;  // 32 blocks per partition
-  constexpr int BPW = NB / kDecWaves;    // 8 blocks per wave
-  constexpr int INFL = 4;                // blocks whose K loads are in flight together
+  constexpr int KST = D / 32;            // k-steps of q.K^T (16x16x32)
+  constexpr int CH = D / 8;              // 16-byte chunks per K/V row
+  constexpr int ROWS = 64 / CH;          // V rows per 16-byte load instruction
+  constexpr int VST = kDecBS / ROWS;     // V load instructions per block
+  // the reference max is raised only when it grows by more than TAU (log2
+  // units); probabilities stay below 2^TAU and O is rescaled rarely
+  constexpr float TAU = 8.0f;
   static_assert(GP % 4 == 0 && GP <= 16, "padded group");
-  // scores / probabilities [token][head]; reused as the cross-wave merge buffer
-  constexpr int SC_FLOATS = kDecPart * GP;
-  constexpr int OB_FLOATS = kDecWaves * GP * D;
-  __shared__ __attribute__((aligned(16))) float sbuf[SC_FLOATS > OB_FLOATS ? SC_FLOATS : OB_FLOATS];
-  __shared__ float red[kDecWaves][GP];
-  __shared__ float stat_m[GP], stat_l[GP];
+  // wave-private exchange: probabilities [token][head], block maxima and
+  // final sums per head
+  __shared__ __attribute__((aligned(16))) float xp[kDecBS * GP];
+  __shared__ __attribute__((aligned(16))) float xm[2 * GP];
 
   const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int ctx = p.context_lens[s];
   const int group = p.group;
   const int head0 = kvh * group;
@@ -62,8 +64,8 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeParams p)
     // empty context: o = 0, lse = -inf (written once, by partition 0)
     if (part == 0) {
       T* og = (T*)p.o + ((int64_t)s * p.h_q + head0) * D;
-      for (int i = tid; i < group * D; i += 256) og[i] = (T)0.f;
-      if (p.lse != nullptr && tid < group) p.lse[(int64_t)s * p.h_q + head0 + tid] = -INFINITY;
+      for (int i = lane; i < group * D; i += 64) og[i] = (T)0.f;
+      if (p.lse != nullptr && lane < group) p.lse[(int64_t)s * p.h_q + head0 + lane] = -INFINITY;
     }
     return;
   }
@@ -73,183 +75,160 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeParams p)
   const int nblk = (ntok + kDecBS - 1) / kDecBS;
   const int nparts = (ctx + kDecPart - 1) / kDecPart;
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq + tok0 / kDecBS;
-  const T* kc = (const T*)p.k_cache;
-  const T* vc = (const T*)p.v_cache;
+  const char* kc = (const char*)p.k_cache;
+  const char* vc = (const char*)p.v_cache;
+  const int64_t blk_bytes = (int64_t)kDecBS * D * 2;
+  const float c = p.scale_log2;
 
-  // ---- query heads as the A operand (rows = heads, zero padded) ----
-  u32x4 qa[D / 32];
+  // query heads as the A operand of S = Q K^T (rows = heads, zero padded)
+  u32x4 qa[KST];
   {
     const int g = lane & 15;
     const T* qg = (const T*)p.q + ((int64_t)s * p.h_q + head0 + g) * D + (lane >> 4) * 8;
 #pragma unroll
-    for (int st = 0; st < D / 32; ++st) {
+    for (int st = 0; st < KST; ++st) {
       qa[st] = u32x4{0, 0, 0, 0};
       if (g < group) qa[st] = *(const u32x4*)(qg + 32 * st);
     }
   }
+  // per-lane byte offsets within a (block, kv head) tile of 16 x D
+  //   K, B operand: token lane % 16, d = 32 st + 8 (lane / 16)
+  //   V, for the vector products: token ROWS st + lane / CH, d = 8 (lane % CH)
+  const uint32_t kl = (uint32_t)((lane & 15) * D + (lane >> 4) * 8) * 2u;
+  const int vrow = lane / CH, vch = lane % CH;
+  const uint32_t vl = (uint32_t)(vrow * D + vch * 8) * 2u;
 
-  // ---- phase A: scores ----
+  u32x4 kr[RING][KST], vr[RING][VST];
+  auto issue = [&](int lb, int slot) {
+    const int64_t phys = table[lb];
+    const char* kb = kc + (phys * p.h_kv + kvh) * blk_bytes + kl;
+    const char* vb = vc + (phys * p.h_kv + kvh) * blk_bytes + vl;
 #pragma unroll
-  for (int i0 = 0; i0 < BPW; i0 += INFL) {
-    u32x4 kr[INFL][D / 32];
-    int lbs[INFL];
+    for (int st = 0; st < KST; ++st) kr[slot][st] = *(const u32x4*)(kb + st * 64);
 #pragma unroll
-    for (int j = 0; j < INFL; ++j) {
-      const int lb = wave * BPW + i0 + j;
-      lbs[j] = lb;
-      if (lb < nblk) {
-        const int64_t phys = table[lb];
-        const T* kb = kc + (phys * p.h_kv + kvh) * (kDecBS * D) + (lane & 15) * D + (lane >> 4) * 8;
-#pragma unroll
-        for (int st = 0; st < D / 32; ++st) kr[j][st] = *(const u32x4*)(kb + 32 * st);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < INFL; ++j) {
-      const int lb = lbs[j];
-      if (lb < nblk) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < D / 32; ++st) acc = TT::mma16(qa[st], kr[j][st], acc);
-        // lane holds token lb*16 + lane%16, heads (lane/16)*4 + 0..3
-        const int t = lb * kDecBS + (lane & 15);
-        const bool tv = (tok0 + t) < ctx;
-        const int g0 = (lane >> 4) * 4;
-        if (g0 < GP) {
-          f32x4 sv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sv[r] = tv ? acc[r] * p.scale_log2 : -INFINITY;
-          *(f32x4*)(sbuf + t * GP + g0) = sv;
-        }
-      }
-    }
-  }
-  __syncthreads();
+    for (int st = 0; st < VST; ++st) vr[slot][st] = *(const u32x4*)(vb + st * ROWS * D * 2);
+  };
 
-  // ---- partition max per head ----
-  {
-    float mx[GP];
+  // running state: reference max per head (identical in all lanes),
+  // per-lane partial sums of probabilities and output partials
+  float m_ref[GP];
+  float l_part[4];    // heads (lane/16)*4 + r, over this lane's tokens
+  float oa[GP][8];    // heads x 8 d of column chunk vch, over tokens of row vrow
 #pragma unroll
-    for (int g = 0; g < GP; ++g) mx[g] = -INFINITY;
-    for (int t = tid; t < ntok; t += 256) {
-#pragma unroll
-      for (int g4 = 0; g4 < GP; g4 += 4) {
-        const f32x4 v = *(const f32x4*)(sbuf + t * GP + g4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx[g4 + r] = fmaxf(mx[g4 + r], v[r]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], sh));
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < GP; ++g) red[wave][g] = mx[g];
-    }
-    __syncthreads();
-    if (tid < GP) {
-      float m = red[0][tid];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) m = fmaxf(m, red[w][tid]);
-      stat_m[tid] = m;
-    }
-    __syncthreads();
-  }
-
-  // ---- probabilities in place, partition sum per head ----
-  {
-    float sm[GP], m[GP];
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      sm[g] = 0.f;
-      m[g] = stat_m[g];
-    }
-    for (int t = tid; t < ntok; t += 256) {
-#pragma unroll
-      for (int g4 = 0; g4 < GP; g4 += 4) {
-        f32x4 v = *(const f32x4*)(sbuf + t * GP + g4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = fast_exp2(v[r] - m[g4 + r]);
-          sm[g4 + r] += v[r];
-        }
-        *(f32x4*)(sbuf + t * GP + g4) = v;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) sm[g] += __shfl_xor(sm[g], sh);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < GP; ++g) red[wave][g] = sm[g];
-    }
-    __syncthreads();
-    if (tid < GP) {
-      float l = red[0][tid];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) l += red[w][tid];
-      stat_l[tid] = l;
-    }
-    // (probabilities written above are read after the next barrier)
-  }
-
-  // ---- phase B: O_part = sum_t p_t v_t ----
-  const int r4 = lane >> 4;   // token row within a group of 4
-  const int c16 = lane & 15;  // 8-element column chunk of d (D = 128) ...
-  constexpr int CH = D / 8;   // ... chunks per row: 16 (D=128) or 8 (D=64)
-  constexpr int ROWS = 64 / CH;   // token rows per load instruction: 4 or 8
-  float oa[GP][8];
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
+  for (int g = 0; g < GP; ++g) {
+    m_ref[g] = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) oa[g][e] = 0.f;
-  __syncthreads();
-  {
-    const int cch = lane % CH;
-    const int rr = lane / CH;
-#pragma unroll 2
-    for (int i = 0; i < BPW; ++i) {
-      const int lb = wave * BPW + i;
-      if (lb >= nblk) break;
-      const int64_t phys = table[lb];
-      const T* vb = vc + (phys * p.h_kv + kvh) * (kDecBS * D) + cch * 8;
-      u32x4 vv[kDecBS / ROWS];
+  }
 #pragma unroll
-      for (int st = 0; st < kDecBS / ROWS; ++st) {
-        const int tok = st * ROWS + rr;
-        vv[st] = u32x4{0, 0, 0, 0};
-        if (tok0 + lb * kDecBS + tok < ctx) vv[st] = *(const u32x4*)(vb + tok * D);
+  for (int r = 0; r < 4; ++r) l_part[r] = 0.f;
+
+  auto process = [&](int lb, int slot) {
+    // ---- scores of 16 tokens x (up to 16) heads on the matrix cores ----
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KST; ++st) acc = TT::mma16(qa[st], kr[slot][st], acc);
+    // lane holds token lb*16 + lane%16, heads (lane/16)*4 + r; tokens past
+    // the context are replaced by -inf (never multiplied)
+    const bool tv = tok0 + lb * kDecBS + (lane & 15) < ctx;
+    float sc[4], bm[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = tv ? acc[r] : -INFINITY;
+      bm[r] = sc[r];
+    }
+    // block max per head over the 16 tokens (lanes of one 16-lane row)
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bm[r] = fmaxf(bm[r], __shfl_xor(bm[r], sh, 16));
+    // every lane learns the block max of every head through LDS
+    const int grow_row = lane >> 4;
+    if ((lane & 15) == 0 && grow_row * 4 < GP) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xm[grow_row * 4 + r] = bm[r] * c;
+    }
+    // (all lanes see the same block maxima, so `grow` is wave-uniform)
+    float alpha[GP];
+    bool any_grow = false;
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      const float t = xm[g];
+      const bool grow = t > m_ref[g] + TAU;
+      alpha[g] = fast_exp2(grow ? m_ref[g] - t : 0.f);
+      m_ref[g] = grow ? t : m_ref[g];
+      any_grow = any_grow || grow;
+    }
+    if (any_grow) {
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oa[g][e] *= alpha[g];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (grow_row * 4 + r < GP) l_part[r] *= alpha[grow_row * 4 + r];
+    }
+    float mine_m[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mine_m[r] = (grow_row * 4 + r < GP) ? m_ref[grow_row * 4 + r] : 0.f;
+    // probabilities relative to the reference, to LDS as [token][head]
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mm = (mine_m[r] == -INFINITY) ? 0.f : mine_m[r];
+      pr[r] = fast_exp2(fmaf(sc[r], c, -mm));
+      l_part[r] += pr[r];
+    }
+    if (grow_row * 4 < GP)
+      *(f32x4*)(xp + (lane & 15) * GP + grow_row * 4) = f32x4{pr[0], pr[1], pr[2], pr[3]};
+    // ---- O += p v on the vector ALUs (V rows past the context are zero) ----
+    const bool last = (tok0 + (lb + 1) * kDecBS > ctx);
+#pragma unroll
+    for (int st = 0; st < VST; ++st) {
+      const int tok = st * ROWS + vrow;
+      u32x4 vv = vr[slot][st];
+      if (last && tok0 + lb * kDecBS + tok >= ctx) vv = u32x4{0, 0, 0, 0};
+      float vf[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vf[2 * w] = TT::lo(vv[w]);
+        vf[2 * w + 1] = TT::hi(vv[w]);
       }
 #pragma unroll
-      for (int st = 0; st < kDecBS / ROWS; ++st) {
-        const int t = lb * kDecBS + st * ROWS + rr;
-        float vf[8];
+      for (int g4 = 0; g4 < GP; g4 += 4) {
+        const f32x4 pv = *(const f32x4*)(xp + tok * GP + g4);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          vf[2 * w] = TT::lo(vv[st][w]);
-          vf[2 * w + 1] = TT::hi(vv[st][w]);
-        }
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int g4 = 0; g4 < GP; g4 += 4) {
-          // tokens past the context have p = 0 exactly and v = 0
-          const f32x4 pv = (tok0 + t < ctx) ? *(const f32x4*)(sbuf + t * GP + g4)
-                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int e = 0; e < 8; ++e) oa[g4 + r][e] = fmaf(pv[r], vf[e], oa[g4 + r][e]);
+      }
+    }
+  };
+
+  // ---- stream the partition's blocks through a ring of RING loads ----
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+  for (int j = 0; j < RING; ++j)
+    if (j < nblk) issue(j, j);
+  for (int i = 0; i < nblk; i += RING) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) oa[g4 + r][e] = fmaf(pv[r], vf[e], oa[g4 + r][e]);
-        }
+    for (int j = 0; j < RING; ++j) {
+      const int lb = i + j;
+      if (lb < nblk) {
+        process(lb, j);
+        if (lb + RING < nblk) issue(lb + RING, j);
       }
     }
   }
-  (void)r4;
-  (void)c16;
 
-  // ---- merge: lanes sharing a d chunk, then waves ----
+  // ---- merge lanes: sums per head over the 16 tokens of a row, O over rows ----
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1) l_part[r] += __shfl_xor(l_part[r], sh, 16);
+  if ((lane & 15) == 0 && (lane >> 4) * 4 < GP) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xm[GP + (lane >> 4) * 4 + r] = l_part[r];
+  }
 #pragma unroll
   for (int g = 0; g < GP; ++g)
 #pragma unroll
@@ -258,33 +237,28 @@ __global__ __launch_bounds__(256) void paged_decode_split_kernel(DecodeParams p)
       for (int sh = CH; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
       oa[g][e] = x;
     }
-  __syncthreads();  // all waves are done reading probabilities
   if (lane < CH) {
+    for (int g = 0; g < group; ++g) {
+      const float l = xm[GP + g];
+      const int head = head0 + g;
+      if (nparts == 1) {
+        const float inv = 1.f / l;
+        T* og = (T*)p.o + ((int64_t)s * p.h_q + head) * D + lane * 8;
+        u32x4 w;
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      float* dst = sbuf + (wave * GP + g) * D + lane * 8;
-      *(f32x4*)(dst) = f32x4{oa[g][0], oa[g][1], oa[g][2], oa[g][3]};
-      *(f32x4*)(dst + 4) = f32x4{oa[g][4], oa[g][5], oa[g][6], oa[g][7]};
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < group * D; idx += 256) {
-    const int g = idx / D, dd = idx - g * D;
-    float acc = sbuf[(0 * GP + g) * D + dd];
-#pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) acc += sbuf[(w * GP + g) * D + dd];
-    const int head = head0 + g;
-    if (nparts == 1) {
-      const float l = stat_l[g];
-      ((T*)p.o)[((int64_t)s * p.h_q + head) * D + dd] = (T)(acc / l);
-      if (p.lse != nullptr && dd == 0)
-        p.lse[(int64_t)s * p.h_q + head] = (stat_m[g] + __log2f(l)) * kLn2;
-    } else {
-      const int64_t slot = ((int64_t)s * p.h_q + head) * p.max_parts + part;
-      p.ws_o[slot * D + dd] = acc;
-      if (dd == 0) {
-        p.ws_ml[slot * 2 + 0] = stat_m[g];
-        p.ws_ml[slot * 2 + 1] = stat_l[g];
+        for (int k = 0; k < 4; ++k) w[k] = TT::pack2(oa[g][2 * k] * inv, oa[g][2 * k + 1] * inv);
+        *(u32x4*)og = w;
+        if (p.lse != nullptr && lane == 0)
+          p.lse[(int64_t)s * p.h_q + head] = (m_ref[g] + __log2f(l)) * kLn2;
+      } else {
+        const int64_t slot = ((int64_t)s * p.h_q + head) * p.max_parts + part;
+        float* dst = p.ws_o + slot * D + lane * 8;
+        *(f32x4*)dst = f32x4{oa[g][0], oa[g][1], oa[g][2], oa[g][3]};
+        *(f32x4*)(dst + 4) = f32x4{oa[g][4], oa[g][5], oa[g][6], oa[g][7]};
+        if (lane == 0) {
+          p.ws_ml[slot * 2 + 0] = m_ref[g];
+          p.ws_ml[slot * 2 + 1] = l;
+        }
       }
     }
   }
@@ -329,7 +303,8 @@ int decode_max_parts(int max_context_len) {
 template <typename TT, int D, int GP>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.max_parts, p.h_kv, p.num_seqs);
-  hipLaunchKernelGGL((paged_decode_split_kernel<TT, D, GP>), grid, dim3(256), 0, stream, p);
+  constexpr int RING = GP <= 4 ? 3 : 2;
+  hipLaunchKernelGGL((paged_decode_split_kernel<TT, D, GP, RING>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.max_parts > 1) {

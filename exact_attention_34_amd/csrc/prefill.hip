@@ -283,9 +283,10 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       u32x4 opnd[NSLOT];
       opnd[0] = fetch(0);
       opnd[1] = fetch(1);
+      opnd[2] = fetch(2);
 #pragma unroll
       for (int i = 0; i < NSLOT; ++i) {
-        if (i + 2 < NSLOT) opnd[i + 2] = fetch(i + 2);
+        if (i + 3 < NSLOT) opnd[i + 3] = fetch(i + 3);
         if (i < NQK) {
           const int sub = i / NS, s = i % NS;
           if (s == 0) {
