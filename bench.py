@@ -142,8 +142,8 @@ def main():
     tab, ctx = dec.block_table.to(dev), dec.context_lens.to(dev)
     mcl = 8192
     dout = torch.empty_like(dq)
-    ws = torch.empty(max(1, ea.paged_attn_decode_workspace_size(dq.shape[0], dq.shape[1], 128,
-                                                                mcl)),
+    ws = torch.empty(max(1, ea.paged_attn_decode_workspace_size(dq.shape[0], dq.shape[1],
+                                                                kc.shape[1], 128, mcl)),
                      dtype=torch.uint8, device=dev)
     dec_bytes = workloads.decode_bytes(dec.context_lens.numpy(), 8, 128)
 

@@ -62,7 +62,7 @@ def lib():
                            i32, i32, i32, i32, i32, i32,
                            i64p, i64p, i64p, i64p, f32, i32, vp]
     L.paged_attn_decode_workspace_size.restype = ctypes.c_size_t
-    L.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.paged_attn_decode.restype = i32
     L.paged_attn_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, i32, i32,
@@ -137,9 +137,10 @@ def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=F
     return out
 
 
-def paged_attn_decode_workspace_size(num_seqs, h_q, head_dim, max_context_len):
+def paged_attn_decode_workspace_size(num_seqs, h_q, h_kv, head_dim, max_context_len):
     """Bytes of workspace :func:`paged_attn_decode` needs (0 if none)."""
-    return int(lib().paged_attn_decode_workspace_size(num_seqs, h_q, head_dim, max_context_len))
+    return int(lib().paged_attn_decode_workspace_size(num_seqs, h_q, h_kv, head_dim,
+                                                       max_context_len))
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len,
@@ -182,7 +183,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_contex
     if lse is not None and (lse.shape != (S, Hq) or lse.dtype != torch.float32
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [S][Hq] tensor")
-    need = paged_attn_decode_workspace_size(S, Hq, d, int(max_context_len))
+    need = paged_attn_decode_workspace_size(S, Hq, Hkv, d, int(max_context_len))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -12,9 +12,9 @@
 namespace attn {
 hipError_t launch_prefill(int dtype, int head_dim, bool causal, const FwdParams& p,
                           hipStream_t stream);
-hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream);
-size_t decode_workspace_bytes(int num_seqs, int h_q, int head_dim, int max_context_len);
-int decode_max_parts(int max_context_len);
+hipError_t launch_decode(int dtype, const DecodeParams& p, int max_context_len, hipStream_t stream);
+size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int max_context_len);
+int decode_waves(int num_seqs, int h_kv, int max_context_len);
 }  // namespace attn
 
 namespace {
@@ -123,8 +123,9 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
   }
 }
 
-size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int head_dim, int max_context_len) {
-  return attn::decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len);
+size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int h_kv, int head_dim,
+                                        int max_context_len) {
+  return attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
 }
 
 int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
@@ -167,7 +168,7 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u))
       return fail(ATTN_ERR_ALIGN, "paged_attn_decode: block_table, context_lens and lse must be 4-byte aligned");
-    const size_t need = attn::decode_workspace_bytes(num_seqs, h_q, head_dim, max_context_len);
+    const size_t need = attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
     if (need > 0) {
       if (workspace == nullptr || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE,
@@ -176,7 +177,7 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
       if (!aligned16(workspace))
         return fail(ATTN_ERR_ALIGN, "paged_attn_decode: workspace must be 16-byte aligned");
     }
-    if ((int64_t)num_seqs > 65535 || h_kv > 65535)
+    if ((int64_t)num_seqs > 65535 || h_q > 65535)
       return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: too many sequences or heads for one launch");
 
     attn::DecodeParams p{};
@@ -193,17 +194,18 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
     p.group = h_q / h_kv;
     p.head_dim = head_dim;
     p.max_blocks_per_seq = max_blocks_per_seq;
-    p.max_parts = attn::decode_max_parts(max_context_len);
     p.scale_log2 = softmax_scale * attn::kLog2e;
     if (need > 0) {
-      const int64_t slots = (int64_t)num_seqs * h_q * p.max_parts;
+      const int64_t slots =
+          (int64_t)attn::decode_waves(num_seqs, h_kv, max_context_len) * 2 * (h_q / h_kv);
       p.ws_o = static_cast<float*>(workspace);
       p.ws_ml = p.ws_o + slots * head_dim;
     }
     if (debug_enabled())
-      std::fprintf(stderr, "[attn] paged_attn_decode dtype=%d seqs=%d hq=%d hkv=%d d=%d parts=%d\n",
-                   dtype, num_seqs, h_q, h_kv, head_dim, p.max_parts);
-    hipError_t e = attn::launch_decode(dtype, p, reinterpret_cast<hipStream_t>(stream));
+      std::fprintf(stderr, "[attn] paged_attn_decode dtype=%d seqs=%d hq=%d hkv=%d d=%d waves=%d\n",
+                   dtype, num_seqs, h_q, h_kv, head_dim,
+                   attn::decode_waves(num_seqs, h_kv, max_context_len));
+    hipError_t e = attn::launch_decode(dtype, p, max_context_len, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
       return fail(ATTN_ERR_HIP, std::string("paged_attn_decode: launch failed: ") + hipGetErrorString(e));
     return ATTN_OK;

@@ -44,6 +44,11 @@ struct BF16 {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
   }
+  // acc + a.x * b.x + a.y * b.y over packed pairs, fp32 accumulation
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+  }
   // widen the low / high 16-bit half of a dword to fp32 (exact)
   __device__ static inline float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
   __device__ static inline float hi(uint32_t w) {
@@ -69,6 +74,10 @@ struct F16 {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
   }
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                  false);
+  }
   __device__ static inline float lo(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
   }
@@ -87,6 +96,36 @@ __device__ inline uint32_t join_hi16(uint32_t a, uint32_t b) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Orders a wave's LDS writes before its later LDS reads of data other lanes
+// wrote (possibly through a different element type).  The hardware executes
+// one wave's LDS operations in order; this only stops the compiler from
+// moving the reads above the writes.
+__device__ inline void lds_order() { asm volatile("" ::: "memory"); }
+
+// Value of `v` held by the lane that DPP control CTRL selects in this lane's row.
+template <int CTRL>
+__device__ inline float dpp_src(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xf, 0xf, false));
+}
+// max / sum of a value over the 16 lanes of its DPP row (lanes 16k .. 16k+15):
+// xor 1, xor 2 within quads (quad_perm [1,0,3,2], [2,3,0,1]), then the
+// half-row mirror and the row mirror.
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, dpp_src<0xB1>(x));
+  x = fmaxf(x, dpp_src<0x4E>(x));
+  x = fmaxf(x, dpp_src<0x141>(x));
+  x = fmaxf(x, dpp_src<0x140>(x));
+  return x;
+}
+__device__ inline float row16_sum(float x) {
+  x += dpp_src<0xB1>(x);
+  x += dpp_src<0x4E>(x);
+  x += dpp_src<0x141>(x);
+  x += dpp_src<0x140>(x);
+  return x;
+}
 
 // max / sum of a value over the lane pair (l, l xor 32): v_permlane32_swap of
 // x with itself leaves {x[l % 32], x[l % 32 + 32]} in the two results.
@@ -147,10 +186,10 @@ struct DecodeParams {
   const int32_t* context_lens;
   void* o;
   float* lse;
-  float* ws_o;    // [num_seqs][h_q][max_parts][head_dim]
-  float* ws_ml;   // [num_seqs][h_q][max_parts][2]  (max in log2 units, sum)
+  float* ws_o;    // [waves][2][group][head_dim] partial outputs
+  float* ws_ml;   // [waves][2][group][2]  (max in log2 units, sum)
   int num_seqs, h_q, h_kv, group, head_dim;
-  int max_blocks_per_seq, max_parts;
+  int max_blocks_per_seq;
   float scale_log2;
 };
 

@@ -3,44 +3,77 @@
 // "Chapter 3 Advanced principles", section 3.0: fixed-size KV blocks and a
 // per-sequence table of physical block ids; shared prefixes are repeated ids).
 //
-// Split kernel, one workgroup per (context partition of 512 tokens, KV head,
-// sequence); the GQA group of query heads that read this KV head is handled
-// together, so every K/V byte is fetched from HBM once per partition:
-//   phase A  each wave takes 8 blocks of 16 tokens; for every block the 16 x d
-//            K tile is read straight from HBM in the B-operand layout of
-//            v_mfma_f32_16x16x32 (token = lane % 16) and multiplied by the
-//            query heads (A operand rows, zero padded to 16); the scaled
-//            scores go to LDS;
-//   softmax  the partition's max and sum per head are reduced through LDS
-//            (the two-pass form of the definition, restricted to the
-//            partition); scores become probabilities in place;
-//   phase B  each wave re-walks its blocks reading V with fully coalesced
-//            16-byte loads (4 tokens x 256 bytes per instruction) and
-//            accumulates p * v in fp32 on the vector ALUs;
-//   merge    lanes, then waves, are summed in a fixed order through LDS.  A
-//            sequence with a single partition is normalised and written here;
-//            otherwise the unnormalised partial output with its (max, sum) goes
-//            to the workspace.
-// Combine kernel, one workgroup per (head, sequence): the partitions are merged
-// by their log-sum-exp -- the same rescaling by exp(m_p - M) that the online
-// softmax applies between key blocks.
+// Work decomposition (split-K over a flattened block list).  A "unit" is one
+// (sequence, KV head) pair; it owns ceil(context / 16) blocks and serves the
+// GQA group of query heads that read that KV head, so every K/V byte is
+// fetched once.  All units' blocks, in (sequence, KV head, block) order, form
+// one list of T blocks that is cut into W equal contiguous ranges, one per
+// persistent wave.  A wave streams its range through a ring of RING blocks of
+// K and V loads that runs on across unit boundaries, so the memory pipeline
+// fills once per wave instead of once per unit.
+//   * a unit that lies entirely inside one wave's range is finished there:
+//     normalised output and log-sum-exp are written directly;
+//   * a unit cut by range boundaries leaves one partial (unnormalised O, max,
+//     sum) per wave it touches -- at most two per wave: the head segment
+//     (unit begun in an earlier range) and the tail segment (unit continued in
+//     a later range);
+//   * the combine kernel merges a cut unit's partials by their log-sum-exp,
+//     the same rescaling by exp(m_p - M) that the online softmax applies
+//     between key blocks.
+// Per block: q.K^T for 16 tokens on the matrix cores (v_mfma_f32_16x16x32,
+// query heads as A rows zero padded to 16, K read straight from memory in the
+// B-operand layout), online softmax with a lazily raised reference max, and
+// P.V on the vector ALUs as packed dot products over token pairs.
 //
 // Tokens at or past the context length are never multiplied: their scores are
-// replaced (not scaled) by -inf and their V rows are not loaded, so whatever a
-// partially filled block holds past the end cannot reach the output.  Nothing
-// depends on physical block ids except addresses, so results are bit-identical
-// under any block table.
+// replaced (not scaled) by -inf and their V rows are zeroed before use, so
+// whatever a partially filled block holds past the end cannot reach the
+// output.  Nothing depends on physical block ids except addresses, so results
+// are bit-identical under any block table.
 #include "common.h"
 
 namespace attn {
 
-constexpr int kDecBS = 16;     // tokens per KV block
-constexpr int kDecPart = 512;  // tokens per partition
+constexpr int kDecBS = 16;          // tokens per KV block
+constexpr int kDecMaxWaves = 2048;  // persistent waves (8 per CU on 256 CUs)
+
+// Blocks of a sequence (one unit per KV head).
+__device__ inline int seq_blocks(int ctx) { return ctx > 0 ? (ctx + kDecBS - 1) / kDecBS : 0; }
+
+// Range of wave w in the flattened block list: [w T / W, (w + 1) T / W).
+__device__ inline int64_t range_start(int w, int64_t T, int W) { return (int64_t)w * T / W; }
+
+// The wave whose range holds block b (0 <= b < T): the last w whose range
+// starts at or before b.
+__device__ inline int wave_of(int64_t b, int64_t T, int W) {
+  int w = (int)(b * W / T);   // range_start(w) <= b already
+  while (w + 1 < W && range_start(w + 1, T, W) <= b) ++w;
+  return w;
+}
+
+// Total blocks over all sequences and the blocks of sequences before `s`,
+// reduced across the 64 lanes of the calling wave.
+__device__ inline void seq_block_sums(const DecodeParams& p, int s, int lane, int64_t& before,
+                                      int64_t& total) {
+  before = 0;
+  total = 0;
+  for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+    const int ss = s0 + lane;
+    const int nb = (ss < p.num_seqs) ? seq_blocks(p.context_lens[ss]) : 0;
+    int a = (ss < s) ? nb : 0, t = nb;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) {
+      a += __shfl_xor(a, sh);
+      t += __shfl_xor(t, sh);
+    }
+    before += a;
+    total += t;
+  }
+}
 
 template <typename TT, int D, int GP, int RING>
 __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) {
   typedef typename TT::elem T;
-  constexpr int NB = kDecPart / kDecBS;  // 32 blocks per partition
   constexpr int KST = D / 32;            // k-steps of q.K^T (16x16x32)
   constexpr int CH = D / 8;              // 16-byte chunks per K/V row
   constexpr int ROWS = 64 / CH;          // V rows per 16-byte load instruction
@@ -49,288 +82,386 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
   // units); probabilities stay below 2^TAU and O is rescaled rarely
   constexpr float TAU = 8.0f;
   static_assert(GP % 4 == 0 && GP <= 16, "padded group");
-  // wave-private exchange: probabilities [token][head], block maxima and
-  // final sums per head
-  __shared__ __attribute__((aligned(16))) float xp[kDecBS * GP];
+  // wave-private exchange: rounded probabilities [head][token], rescale
+  // factors, final max and sums per head
+  __shared__ __attribute__((aligned(16))) uint16_t xp16[GP * kDecBS];
   __shared__ __attribute__((aligned(16))) float xm[2 * GP];
 
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int w = blockIdx.x, W = gridDim.x;
   const int lane = threadIdx.x;
-  const int ctx = p.context_lens[s];
   const int group = p.group;
-  const int head0 = kvh * group;
+  const float c = p.scale_log2;
 
-  if (ctx <= 0) {
-    // empty context: o = 0, lse = -inf (written once, by partition 0)
-    if (part == 0) {
-      T* og = (T*)p.o + ((int64_t)s * p.h_q + head0) * D;
-      for (int i = lane; i < group * D; i += 64) og[i] = (T)0.f;
-      if (p.lse != nullptr && lane < group) p.lse[(int64_t)s * p.h_q + head0 + lane] = -INFINITY;
+  int64_t unused_before, total_seq_blocks;
+  seq_block_sums(p, 0, lane, unused_before, total_seq_blocks);
+  const int64_t nlist = total_seq_blocks * p.h_kv;   // blocks in the list
+  if (nlist == 0) return;
+  const int64_t b0 = range_start(w, nlist, W), b1 = range_start(w + 1, nlist, W);
+  if (b0 >= b1) return;
+
+  // position in the unit list: unit (s, kvh), its blocks and context, the
+  // list position of its first block and the block within it
+  struct Cursor {
+    int s, kvh, nblk, ctx;
+    int64_t ustart;
+    int lb;
+  };
+  auto seek = [&](int64_t b) {
+    Cursor cu{};
+    int64_t pos = 0;
+    for (int s = 0;; ++s) {
+      const int ctx = p.context_lens[s];
+      const int nb = seq_blocks(ctx);
+      const int64_t span = (int64_t)nb * p.h_kv;
+      if (b < pos + span) {
+        cu.s = s;
+        cu.kvh = (int)((b - pos) / nb);
+        cu.nblk = nb;
+        cu.ctx = ctx;
+        cu.ustart = pos + (int64_t)cu.kvh * nb;
+        cu.lb = (int)(b - cu.ustart);
+        return cu;
+      }
+      pos += span;
     }
-    return;
-  }
-  const int tok0 = part * kDecPart;
-  if (tok0 >= ctx) return;
-  const int ntok = min(kDecPart, ctx - tok0);
-  const int nblk = (ntok + kDecBS - 1) / kDecBS;
-  const int nparts = (ctx + kDecPart - 1) / kDecPart;
-  const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq + tok0 / kDecBS;
+  };
+  auto advance = [&](Cursor& cu) {
+    if (++cu.lb < cu.nblk) return;
+    cu.ustart += cu.nblk;
+    cu.lb = 0;
+    if (++cu.kvh < p.h_kv) return;
+    cu.kvh = 0;
+    do {   // next sequence with blocks (past the end: a harmless dummy unit)
+      ++cu.s;
+      cu.ctx = (cu.s < p.num_seqs) ? p.context_lens[cu.s] : 1;
+      cu.nblk = seq_blocks(cu.ctx);
+    } while (cu.nblk == 0);
+  };
+
   const char* kc = (const char*)p.k_cache;
   const char* vc = (const char*)p.v_cache;
   const int64_t blk_bytes = (int64_t)kDecBS * D * 2;
-  const float c = p.scale_log2;
 
-  // query heads as the A operand of S = Q K^T (rows = heads, zero padded)
+  // per-lane byte offsets within a (block, kv head) tile of 16 x D
+  //   K, B operand: token lane % 16, d = 32 st + 8 (lane / 16)
+  //   V, for the vector products: load st brings token
+  //   2 (lane / CH) + (st & 1) + (st >> 1) * 2 ROWS, d = 8 (lane % CH), so that
+  //   loads 2u and 2u+1 hold two adjacent tokens of the same 8 columns
+  const uint32_t kl = (uint32_t)((lane & 15) * D + (lane >> 4) * 8) * 2u;
+  const int vrow = lane / CH;
+  auto vtok = [&](int st) { return 2 * vrow + (st & 1) + (st >> 1) * 2 * ROWS; };
+  const uint32_t vl = (uint32_t)(2 * vrow * D + (lane % CH) * 8) * 2u;
+
+  u32x4 kr[RING][KST], vr[RING][VST];
+  auto issue = [&](const Cursor& cu, int slot) {
+    const int64_t phys = p.block_table[(int64_t)cu.s * p.max_blocks_per_seq + cu.lb];
+    const char* kb = kc + (phys * p.h_kv + cu.kvh) * blk_bytes + kl;
+    const char* vb = vc + (phys * p.h_kv + cu.kvh) * blk_bytes + vl;
+#pragma unroll
+    for (int st = 0; st < KST; ++st) kr[slot][st] = *(const u32x4*)(kb + st * 64);
+#pragma unroll
+    for (int st = 0; st < VST; ++st)
+      vr[slot][st] = *(const u32x4*)(vb + ((st & 1) + (st >> 1) * 2 * ROWS) * D * 2);
+  };
+  // query heads of a unit as the A operand of S = Q K^T (rows = heads, zero padded)
   u32x4 qa[KST];
-  {
+  auto load_q = [&](const Cursor& cu) {
     const int g = lane & 15;
-    const T* qg = (const T*)p.q + ((int64_t)s * p.h_q + head0 + g) * D + (lane >> 4) * 8;
+    const T* qg =
+        (const T*)p.q + ((int64_t)cu.s * p.h_q + cu.kvh * group + g) * D + (lane >> 4) * 8;
 #pragma unroll
     for (int st = 0; st < KST; ++st) {
       qa[st] = u32x4{0, 0, 0, 0};
       if (g < group) qa[st] = *(const u32x4*)(qg + 32 * st);
     }
-  }
-  // per-lane byte offsets within a (block, kv head) tile of 16 x D
-  //   K, B operand: token lane % 16, d = 32 st + 8 (lane / 16)
-  //   V, for the vector products: token ROWS st + lane / CH, d = 8 (lane % CH)
-  const uint32_t kl = (uint32_t)((lane & 15) * D + (lane >> 4) * 8) * 2u;
-  const int vrow = lane / CH, vch = lane % CH;
-  const uint32_t vl = (uint32_t)(vrow * D + vch * 8) * 2u;
-
-  u32x4 kr[RING][KST], vr[RING][VST];
-  auto issue = [&](int lb, int slot) {
-    const int64_t phys = table[lb];
-    const char* kb = kc + (phys * p.h_kv + kvh) * blk_bytes + kl;
-    const char* vb = vc + (phys * p.h_kv + kvh) * blk_bytes + vl;
-#pragma unroll
-    for (int st = 0; st < KST; ++st) kr[slot][st] = *(const u32x4*)(kb + st * 64);
-#pragma unroll
-    for (int st = 0; st < VST; ++st) vr[slot][st] = *(const u32x4*)(vb + st * ROWS * D * 2);
   };
 
-  // running state: reference max per head (identical in all lanes),
-  // per-lane partial sums of probabilities and output partials
-  float m_ref[GP];
-  float l_part[4];    // heads (lane/16)*4 + r, over this lane's tokens
-  float oa[GP][8];    // heads x 8 d of column chunk vch, over tokens of row vrow
+  // running state of the current unit: reference max of the heads of this
+  // lane's 16-lane row (heads (lane/16)*4 + r), per-lane partial sums of the
+  // rounded probabilities, output partials (heads x 8 columns of chunk lane%CH)
+  const int grow_row = lane >> 4;
+  const bool score_lane = grow_row * 4 < GP;
+  float m_ref[4], l_part[4];
+  float oa[GP][8];
+  auto reset = [&]() {
 #pragma unroll
-  for (int g = 0; g < GP; ++g) {
-    m_ref[g] = -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      m_ref[r] = -INFINITY;
+      l_part[r] = 0.f;
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oa[g][e] = 0.f;
-  }
+    for (int g = 0; g < GP; ++g)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) l_part[r] = 0.f;
+      for (int e = 0; e < 8; ++e) oa[g][e] = 0.f;
+  };
 
-  auto process = [&](int lb, int slot) {
+  auto process = [&](const Cursor& cu, int slot) {
     // ---- scores of 16 tokens x (up to 16) heads on the matrix cores ----
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KST; ++st) acc = TT::mma16(qa[st], kr[slot][st], acc);
-    // lane holds token lb*16 + lane%16, heads (lane/16)*4 + r; tokens past
-    // the context are replaced by -inf (never multiplied)
-    const bool tv = tok0 + lb * kDecBS + (lane & 15) < ctx;
-    float sc[4], bm[4];
+    // lane holds token lb*16 + lane%16, heads (lane/16)*4 + r (log2 units);
+    // tokens past the context are replaced by -inf (never multiplied)
+    const int tbase = cu.lb * kDecBS;
+    const bool tv = tbase + (lane & 15) < cu.ctx;
+    float sc[4];
+    bool grow = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[r] = tv ? acc[r] : -INFINITY;
-      bm[r] = sc[r];
+      sc[r] = tv ? acc[r] * c : -INFINITY;
+      grow = grow || (score_lane && sc[r] > m_ref[r] + TAU);
     }
-    // block max per head over the 16 tokens (lanes of one 16-lane row)
+    // ---- rare: a score passed its head's reference by more than TAU ----
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      float alpha[4];
 #pragma unroll
-    for (int sh = 1; sh < 16; sh <<= 1)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bm[r] = fmaxf(bm[r], __shfl_xor(bm[r], sh, 16));
-    // every lane learns the block max of every head through LDS
-    const int grow_row = lane >> 4;
-    if ((lane & 15) == 0 && grow_row * 4 < GP) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) xm[grow_row * 4 + r] = bm[r] * c;
-    }
-    // (all lanes see the same block maxima, so `grow` is wave-uniform)
-    float alpha[GP];
-    bool any_grow = false;
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      const float t = xm[g];
-      const bool grow = t > m_ref[g] + TAU;
-      alpha[g] = fast_exp2(grow ? m_ref[g] - t : 0.f);
-      m_ref[g] = grow ? t : m_ref[g];
-      any_grow = any_grow || grow;
-    }
-    if (any_grow) {
-#pragma unroll
-      for (int g = 0; g < GP; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) oa[g][e] *= alpha[g];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (grow_row * 4 + r < GP) l_part[r] *= alpha[grow_row * 4 + r];
-    }
-    float mine_m[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mine_m[r] = (grow_row * 4 + r < GP) ? m_ref[grow_row * 4 + r] : 0.f;
-    // probabilities relative to the reference, to LDS as [token][head]
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mm = (mine_m[r] == -INFINITY) ? 0.f : mine_m[r];
-      pr[r] = fast_exp2(fmaf(sc[r], c, -mm));
-      l_part[r] += pr[r];
-    }
-    if (grow_row * 4 < GP)
-      *(f32x4*)(xp + (lane & 15) * GP + grow_row * 4) = f32x4{pr[0], pr[1], pr[2], pr[3]};
-    // ---- O += p v on the vector ALUs (V rows past the context are zero) ----
-    const bool last = (tok0 + (lb + 1) * kDecBS > ctx);
-#pragma unroll
-    for (int st = 0; st < VST; ++st) {
-      const int tok = st * ROWS + vrow;
-      u32x4 vv = vr[slot][st];
-      if (last && tok0 + lb * kDecBS + tok >= ctx) vv = u32x4{0, 0, 0, 0};
-      float vf[8];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        vf[2 * w] = TT::lo(vv[w]);
-        vf[2 * w + 1] = TT::hi(vv[w]);
+      for (int r = 0; r < 4; ++r) {
+        const float bm = row16_max(sc[r]);
+        const bool up = bm > m_ref[r] + TAU;
+        alpha[r] = fast_exp2(up ? m_ref[r] - bm : 0.f);
+        m_ref[r] = up ? bm : m_ref[r];
+        l_part[r] *= alpha[r];
       }
+      if ((lane & 15) == 0 && score_lane)
+        *(f32x4*)(xm + grow_row * 4) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
+      lds_order();
 #pragma unroll
       for (int g4 = 0; g4 < GP; g4 += 4) {
-        const f32x4 pv = *(const f32x4*)(xp + tok * GP + g4);
+        const f32x4 a = *(const f32x4*)(xm + g4);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) oa[g4 + r][e] = fmaf(pv[r], vf[e], oa[g4 + r][e]);
+          for (int e = 0; e < 8; ++e) oa[g4 + r][e] *= a[r];
+      }
+    }
+    // probabilities relative to the reference, rounded as they enter P V,
+    // to LDS as [head][token]; l sums the rounded values
+    if (score_lane) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mm = (m_ref[r] == -INFINITY) ? 0.f : m_ref[r];
+        const uint32_t wv = TT::pack2(fast_exp2(sc[r] - mm), 0.f);
+        l_part[r] = TT::sum2(wv, l_part[r]);
+        xp16[(grow_row * 4 + r) * kDecBS + (lane & 15)] = (uint16_t)wv;
+      }
+    }
+    lds_order();
+    // ---- O += p v with packed dot products over token pairs ----
+    const bool last = tbase + kDecBS > cu.ctx;
+#pragma unroll
+    for (int u = 0; u < VST / 2; ++u) {
+      const int t0 = vtok(2 * u);   // t1 = t0 + 1
+      u32x4 va = vr[slot][2 * u], vb2 = vr[slot][2 * u + 1];
+      if (last) {
+        if (tbase + t0 >= cu.ctx) va = u32x4{0, 0, 0, 0};
+        if (tbase + t0 + 1 >= cu.ctx) vb2 = u32x4{0, 0, 0, 0};
+      }
+      uint32_t vp[8];   // (v[t0][d], v[t1][d]) pairs for the 8 columns
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        vp[2 * k] = join_lo16(va[k], vb2[k]);
+        vp[2 * k + 1] = join_hi16(va[k], vb2[k]);
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        const uint32_t pp = *(const uint32_t*)(xp16 + g * kDecBS + t0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oa[g][e] = TT::dot2(vp[e], pp, oa[g][e]);
       }
     }
   };
 
-  // ---- stream the partition's blocks through a ring of RING loads ----
+  // ---- finish this wave's segment [seg_start, seg_end) of a unit ----
+  auto finish = [&](const Cursor& cu, int64_t seg_start, int64_t seg_end) {
 #pragma unroll
-  for (int j = 0; j < RING; ++j)
-    if (j < nblk) issue(j, j);
-  for (int i = 0; i < nblk; i += RING) {
+    for (int r = 0; r < 4; ++r) l_part[r] = row16_sum(l_part[r]);
+    if ((lane & 15) == 0 && score_lane) {
+      *(f32x4*)(xm + grow_row * 4) = f32x4{m_ref[0], m_ref[1], m_ref[2], m_ref[3]};
+      *(f32x4*)(xm + GP + grow_row * 4) = f32x4{l_part[0], l_part[1], l_part[2], l_part[3]};
+    }
+    lds_order();
+    // sum O over the lanes sharing a column chunk
 #pragma unroll
-    for (int j = 0; j < RING; ++j) {
-      const int lb = i + j;
-      if (lb < nblk) {
-        process(lb, j);
-        if (lb + RING < nblk) issue(lb + RING, j);
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = oa[g][e];
+        for (int sh = CH; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
+        oa[g][e] = x;
+      }
+    const bool whole = seg_start == cu.ustart && seg_end == cu.ustart + cu.nblk;
+    // partial slot: 0 = unit begun in an earlier range, 1 = continued later
+    const int jslot = (seg_start > cu.ustart) ? 0 : 1;
+    if (lane < CH) {
+      for (int g = 0; g < group; ++g) {
+        const float l = xm[GP + g], mg = xm[g];
+        const int head = cu.kvh * group + g;
+        if (whole) {
+          const float inv = 1.f / l;
+          T* og = (T*)p.o + ((int64_t)cu.s * p.h_q + head) * D + lane * 8;
+          u32x4 wv;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            wv[k] = TT::pack2(oa[g][2 * k] * inv, oa[g][2 * k + 1] * inv);
+          *(u32x4*)og = wv;
+          if (p.lse != nullptr && lane == 0)
+            p.lse[(int64_t)cu.s * p.h_q + head] = (mg + __log2f(l)) * kLn2;
+        } else {
+          const int64_t slot = ((int64_t)w * 2 + jslot) * group + g;
+          float* dst = p.ws_o + slot * D + lane * 8;
+          *(f32x4*)dst = f32x4{oa[g][0], oa[g][1], oa[g][2], oa[g][3]};
+          *(f32x4*)(dst + 4) = f32x4{oa[g][4], oa[g][5], oa[g][6], oa[g][7]};
+          if (lane == 0) {
+            p.ws_ml[slot * 2 + 0] = mg;
+            p.ws_ml[slot * 2 + 1] = l;
+          }
+        }
       }
     }
-  }
+  };
 
-  // ---- merge lanes: sums per head over the 16 tokens of a row, O over rows ----
+  // ---- stream [b0, b1) through the ring ----
+  const int n = (int)(b1 - b0);
+  Cursor icur = seek(b0);   // next block to load
+  Cursor pcur = icur;       // next block to process
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int sh = 1; sh < 16; sh <<= 1) l_part[r] += __shfl_xor(l_part[r], sh, 16);
-  if ((lane & 15) == 0 && (lane >> 4) * 4 < GP) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) xm[GP + (lane >> 4) * 4 + r] = l_part[r];
-  }
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = oa[g][e];
-      for (int sh = CH; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
-      oa[g][e] = x;
+  for (int j = 0; j < RING; ++j) {
+    if (j < n) {
+      issue(icur, j);
+      advance(icur);
     }
-  if (lane < CH) {
-    for (int g = 0; g < group; ++g) {
-      const float l = xm[GP + g];
-      const int head = head0 + g;
-      if (nparts == 1) {
-        const float inv = 1.f / l;
-        T* og = (T*)p.o + ((int64_t)s * p.h_q + head) * D + lane * 8;
-        u32x4 w;
+  }
+  load_q(pcur);
+  reset();
+  int64_t seg_start = b0;
+  for (int i = 0; i < n; i += RING) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = TT::pack2(oa[g][2 * k] * inv, oa[g][2 * k + 1] * inv);
-        *(u32x4*)og = w;
-        if (p.lse != nullptr && lane == 0)
-          p.lse[(int64_t)s * p.h_q + head] = (m_ref[g] + __log2f(l)) * kLn2;
-      } else {
-        const int64_t slot = ((int64_t)s * p.h_q + head) * p.max_parts + part;
-        float* dst = p.ws_o + slot * D + lane * 8;
-        *(f32x4*)dst = f32x4{oa[g][0], oa[g][1], oa[g][2], oa[g][3]};
-        *(f32x4*)(dst + 4) = f32x4{oa[g][4], oa[g][5], oa[g][6], oa[g][7]};
-        if (lane == 0) {
-          p.ws_ml[slot * 2 + 0] = m_ref[g];
-          p.ws_ml[slot * 2 + 1] = l;
+    for (int j = 0; j < RING; ++j) {
+      const int k = i + j;
+      if (k < n) {
+        process(pcur, j);
+        if (k + RING < n) {
+          issue(icur, j);
+          advance(icur);
+        }
+        if (pcur.lb == pcur.nblk - 1 || k == n - 1) {
+          // the unit, or this wave's range, ends with this block
+          finish(pcur, seg_start, b0 + k + 1);
+          if (k + 1 < n) {
+            advance(pcur);
+            seg_start = b0 + k + 1;
+            load_q(pcur);
+            reset();
+          }
+        } else {
+          advance(pcur);
         }
       }
     }
   }
 }
 
-// Merge the partitions of one (head, sequence): M = max_p m_p,
-// O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p.
+// One workgroup of 64 threads per (query head, sequence).  Sequences with an
+// empty context get o = 0, lse = -inf; units cut by range boundaries get their
+// partials merged: (w0, slot 1) from the wave where the unit starts, then
+// (w, slot 0) for the following waves up to the one where it ends.
 template <typename TT>
-__global__ __launch_bounds__(128) void paged_decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p, int W) {
   typedef typename TT::elem T;
-  const int h = blockIdx.x, s = blockIdx.y;
-  const int ctx = p.context_lens[s];
-  const int nparts = (ctx + kDecPart - 1) / kDecPart;
-  if (nparts <= 1) return;
-  const int64_t base = ((int64_t)s * p.h_q + h) * p.max_parts;
-  float M = -INFINITY;
-  for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, p.ws_ml[(base + pp) * 2]);
-  float L = 0.f;
-  for (int pp = 0; pp < nparts; ++pp)
-    L += fast_exp2(p.ws_ml[(base + pp) * 2] - M) * p.ws_ml[(base + pp) * 2 + 1];
-  for (int dd = threadIdx.x; dd < p.head_dim; dd += blockDim.x) {
-    float acc = 0.f;
-    for (int pp = 0; pp < nparts; ++pp)
-      acc += fast_exp2(p.ws_ml[(base + pp) * 2] - M) * p.ws_o[(base + pp) * p.head_dim + dd];
-    ((T*)p.o)[((int64_t)s * p.h_q + h) * p.head_dim + dd] = (T)(acc / L);
+  const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int D = p.head_dim;
+  const int kvh = h / p.group, g = h - kvh * p.group;
+  T* og = (T*)p.o + ((int64_t)s * p.h_q + h) * D;
+  const int nb = seq_blocks(p.context_lens[s]);
+  if (nb == 0) {
+    for (int d = lane; d < D; d += 64) og[d] = (T)0.f;
+    if (p.lse != nullptr && lane == 0) p.lse[(int64_t)s * p.h_q + h] = -INFINITY;
+    return;
   }
-  if (p.lse != nullptr && threadIdx.x == 0) p.lse[(int64_t)s * p.h_q + h] = (M + __log2f(L)) * kLn2;
+  int64_t before, total;
+  seq_block_sums(p, s, lane, before, total);
+  const int64_t T_ = total * p.h_kv;
+  const int64_t ustart = before * p.h_kv + (int64_t)kvh * nb;
+  const int w0 = wave_of(ustart, T_, W), w1 = wave_of(ustart + nb - 1, T_, W);
+  if (w0 == w1) return;   // finished inside one wave
+  const int np = w1 - w0 + 1;
+  // waves with an empty range (more waves than blocks) hold no partial
+  auto has_part = [&](int k) {
+    return k == 0 || range_start(w0 + k, T_, W) < range_start(w0 + k + 1, T_, W);
+  };
+  auto slot_of = [&](int k) -> int64_t {
+    return k == 0 ? ((int64_t)w0 * 2 + 1) * p.group + g : ((int64_t)(w0 + k) * 2) * p.group + g;
+  };
+  float M = -INFINITY;
+  for (int k = lane; k < np; k += 64)
+    if (has_part(k)) M = fmaxf(M, p.ws_ml[slot_of(k) * 2]);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+  float L = 0.f;
+  for (int k = lane; k < np; k += 64) {
+    if (!has_part(k)) continue;
+    const int64_t sl = slot_of(k);
+    L += fast_exp2(p.ws_ml[sl * 2] - M) * p.ws_ml[sl * 2 + 1];
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) L += __shfl_xor(L, sh);
+  const float inv = 1.f / L;
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.f;
+    for (int k = 0; k < np; ++k) {
+      if (!has_part(k)) continue;
+      const int64_t sl = slot_of(k);
+      acc += fast_exp2(p.ws_ml[sl * 2] - M) * p.ws_o[sl * D + d];
+    }
+    og[d] = (T)(acc * inv);
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[(int64_t)s * p.h_q + h] = (M + __log2f(L)) * kLn2;
 }
 
-size_t decode_workspace_bytes(int num_seqs, int h_q, int head_dim, int max_context_len) {
-  if (num_seqs <= 0 || h_q <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int64_t parts = (max_context_len + kDecPart - 1) / kDecPart;
-  if (parts <= 1) return 0;
-  const int64_t slots = (int64_t)num_seqs * h_q * parts;
+// Persistent waves for these sizes: one per block of the largest possible
+// list, at most kDecMaxWaves.
+int decode_waves(int num_seqs, int h_kv, int max_context_len) {
+  const int64_t tmax = (int64_t)num_seqs * h_kv * ((max_context_len + kDecBS - 1) / kDecBS);
+  return (int)(tmax < kDecMaxWaves ? (tmax > 0 ? tmax : 1) : kDecMaxWaves);
+}
+
+size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int max_context_len) {
+  if (num_seqs <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      h_q % h_kv != 0)
+    return 0;
+  const int64_t slots = (int64_t)decode_waves(num_seqs, h_kv, max_context_len) * 2 * (h_q / h_kv);
   return (size_t)(slots * head_dim * 4 + slots * 2 * 4);
 }
 
-int decode_max_parts(int max_context_len) {
-  return max_context_len <= 0 ? 1 : (max_context_len + kDecPart - 1) / kDecPart;
-}
-
 template <typename TT, int D, int GP>
-static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.max_parts, p.h_kv, p.num_seqs);
+static hipError_t launch_decode_t(const DecodeParams& p, int W, hipStream_t stream) {
   constexpr int RING = GP <= 4 ? 3 : 2;
-  hipLaunchKernelGGL((paged_decode_split_kernel<TT, D, GP, RING>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((paged_decode_split_kernel<TT, D, GP, RING>), dim3(W), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.max_parts > 1) {
-    hipLaunchKernelGGL((paged_decode_combine_kernel<TT>), dim3(p.h_q, p.num_seqs), dim3(128), 0,
-                       stream, p);
-    e = hipGetLastError();
-  }
-  return e;
+  hipLaunchKernelGGL((paged_decode_combine_kernel<TT>), dim3(p.h_q, p.num_seqs), dim3(64), 0,
+                     stream, p, W);
+  return hipGetLastError();
 }
 
 template <typename TT>
-static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeParams& p, int W, hipStream_t stream) {
   const int gp = p.group <= 4 ? 4 : (p.group <= 8 ? 8 : 16);
   if (p.head_dim == 64) {
-    if (gp == 4) return launch_decode_t<TT, 64, 4>(p, stream);
-    if (gp == 8) return launch_decode_t<TT, 64, 8>(p, stream);
-    return launch_decode_t<TT, 64, 16>(p, stream);
+    if (gp == 4) return launch_decode_t<TT, 64, 4>(p, W, stream);
+    if (gp == 8) return launch_decode_t<TT, 64, 8>(p, W, stream);
+    return launch_decode_t<TT, 64, 16>(p, W, stream);
   }
-  if (gp == 4) return launch_decode_t<TT, 128, 4>(p, stream);
-  if (gp == 8) return launch_decode_t<TT, 128, 8>(p, stream);
-  return launch_decode_t<TT, 128, 16>(p, stream);
+  if (gp == 4) return launch_decode_t<TT, 128, 4>(p, W, stream);
+  if (gp == 8) return launch_decode_t<TT, 128, 8>(p, W, stream);
+  return launch_decode_t<TT, 128, 16>(p, W, stream);
 }
 
-hipError_t launch_decode(int dtype, const DecodeParams& p, hipStream_t stream) {
-  if (dtype == 2) return launch_decode_d<BF16>(p, stream);
-  return launch_decode_d<F16>(p, stream);
+hipError_t launch_decode(int dtype, const DecodeParams& p, int max_context_len,
+                         hipStream_t stream) {
+  const int W = decode_waves(p.num_seqs, p.h_kv, max_context_len);
+  if (dtype == 2) return launch_decode_d<BF16>(p, W, stream);
+  return launch_decode_d<F16>(p, W, stream);
 }
 
 }  // namespace attn

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* element types of q, k, v, o and the KV cache */
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -113,9 +113,9 @@ int attn_fwd(int dtype,
 
 /*
  * Bytes of device workspace paged_attn_decode needs for these sizes (the
- * split-K partial results).  Returns 0 for non-positive sizes.
+ * split-K partial results).  Returns 0 for invalid sizes.
  */
-size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int head_dim,
+size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int h_kv, int head_dim,
                                         int max_context_len);
 
 /*
@@ -144,16 +144,19 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int head_dim,
  *                       grid and the workspace size.
  *   max_blocks_per_seq  >= ceil(max_context_len / block_size).
  *   workspace           device memory of at least
- *                       paged_attn_decode_workspace_size(num_seqs, h_q,
+ *                       paged_attn_decode_workspace_size(num_seqs, h_q, h_kv,
  *                       head_dim, max_context_len) bytes, 16-byte aligned,
  *                       owned by the caller; its contents on entry do not
  *                       matter and are garbage on exit.
  *   stream              hipStream_t or NULL.
  *
- * Two kernels are enqueued: a split kernel over (sequence, KV head, context
- * partition) and a combine kernel that merges the partitions' partial
- * results by their log-sum-exp.  Results do not depend on which physical
- * blocks hold the data: the same logical sequence gives bit-identical
+ * Two kernels are enqueued.  The split kernel cuts the list of all
+ * (sequence, KV head, block) triples into equal ranges, one per persistent
+ * wave; a (sequence, KV head) pair finished inside one range is written
+ * there, a pair cut by range boundaries leaves partial results in the
+ * workspace, and the combine kernel merges those by their log-sum-exp (and
+ * writes the empty-context outputs).  Results do not depend on which
+ * physical blocks hold the data: the same logical sequences give bit-identical
  * outputs under any block table.  num_seqs == 0 is a no-op.
  */
 int paged_attn_decode(int dtype,

@@ -35,16 +35,18 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ea.abi_version() == 1
+    assert ea.abi_version() == 2
 
 
 def test_workspace_size():
-    # one partition (<= 512 tokens) needs no workspace
-    assert ea.paged_attn_decode_workspace_size(64, 32, 128, 512) == 0
-    assert ea.paged_attn_decode_workspace_size(0, 32, 128, 8192) == 0
-    # 16 partitions of 512: 64 * 32 * 16 slots of (128 + 2) floats
-    assert ea.paged_attn_decode_workspace_size(64, 32, 128, 8192) == 64 * 32 * 16 * 130 * 4
-    assert ea.paged_attn_decode_workspace_size(2, 4, 64, 513) == 2 * 4 * 2 * 66 * 4
+    # two partial slots per persistent wave, one per query head of a KV head's
+    # group, each (head_dim + 2) floats; at most 2048 waves, at most one wave
+    # per block of the largest possible block list
+    assert ea.paged_attn_decode_workspace_size(0, 32, 8, 128, 8192) == 0
+    assert ea.paged_attn_decode_workspace_size(64, 32, 0, 128, 8192) == 0
+    assert ea.paged_attn_decode_workspace_size(64, 32, 8, 128, 8192) == 2048 * 2 * 4 * 130 * 4
+    # 2 seqs x 1 kv head x ceil(513/16) = 33 blocks -> 66 waves
+    assert ea.paged_attn_decode_workspace_size(2, 4, 1, 64, 513) == 66 * 2 * 4 * 66 * 4
 
 
 FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
@@ -93,7 +95,7 @@ def _dec(dtype=2, q=FAKE, k=FAKE, v=FAKE, table=FAKE, ctx=FAKE, o=FAKE, lse=None
          h_kv=8, d=128, bs=16, mbps=512, mcl=8192, nb=100, scale=0.088, ws=FAKE, ws_bytes=None):
     L = ea.lib()
     if ws_bytes is None:
-        ws_bytes = L.paged_attn_decode_workspace_size(S, h_q, d, mcl)
+        ws_bytes = L.paged_attn_decode_workspace_size(S, h_q, h_kv, d, mcl)
     code = L.paged_attn_decode(dtype, q, k, v, table, ctx, o, lse, S, h_q, h_kv, d, bs, mbps, mcl,
                                nb, scale, ws, ws_bytes, None)
     return code, L.attn_last_error().decode()
