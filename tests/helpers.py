@@ -57,16 +57,19 @@ def assert_close(gpu, ref, dtype, what=""):
     return rep
 
 
-# Log-sum-exp tolerance.  The kernels normalise by the sum of the
-# probabilities *as rounded* for the P V product (so that O's weights sum to
-# exactly what it is divided by); the log of that sum differs from the exact
-# log-sum-exp by at most ln(1 + 2^-(mantissa bits + 1)): 1.95e-3 for bf16,
-# 2.4e-4 for fp16.  fp32 inputs keep fp32 probabilities.  A relative term
-# covers the fp32 accumulation of the q.k dot product: its bound is about
-# d * 2^-24 = 7.6e-6 of sum_i |q_i k_i|, which for random rows exceeds |q.k|
-# by about sqrt(d) = 11, i.e. ~1e-4 of the logit (the stress rows reach
-# logits of ~1e3).
-LSE_TOL = {torch.bfloat16: 2.5e-3, torch.float16: 5e-4, torch.float32: 1e-5}
+# Log-sum-exp tolerance (the subject states tolerances for O only; this one
+# is derived from the arithmetic).  Two terms:
+#  * the kernels normalise by the sum of the probabilities *as rounded* for
+#    the P V product (so that O's weights sum to exactly what it is divided
+#    by); the log of that sum differs from the exact log-sum-exp by at most
+#    ln(1 + 2^-(mantissa bits + 1)): 1.95e-3 for bf16, 2.4e-4 for fp16; fp32
+#    inputs keep fp32 probabilities;
+#  * the fp32 accumulation of q.k: at most d * 2^-24 * scale * sum_i |q_i k_i|,
+#    about 1.1e-3 for a x20 stress key (d = 128, sum_i |q_i k_i| ~ 1.6e3), and
+#    for random rows about sqrt(d) = 11 times |q.k| * d * 2^-24, i.e. ~1e-4 of
+#    the logit itself (the stress rows reach logits of ~1e3).
+# Absolute term = rounding + stress-key accumulation; relative term 1e-4.
+LSE_TOL = {torch.bfloat16: 3.1e-3, torch.float16: 1.4e-3, torch.float32: 1e-5}
 
 
 def assert_lse_close(gpu_lse, ref_lse, dtype, what=""):
