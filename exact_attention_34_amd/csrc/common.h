@@ -25,6 +25,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // fp32 -> 16-bit round-to-nearest-even packing of two values into one dword.
 struct BF16 {
   typedef __bf16 elem;
+  static constexpr bool kIsBf16 = true;
   // 32x32x16: A is 32 rows x 16 k, B is 16 k x 32 columns; each lane holds 8
   // consecutive k values of one row (A) / one column (B).
   __device__ static inline f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -58,6 +59,7 @@ struct BF16 {
 
 struct F16 {
   typedef _Float16 elem;
+  static constexpr bool kIsBf16 = false;
   __device__ static inline f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);

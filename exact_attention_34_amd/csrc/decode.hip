@@ -364,17 +364,21 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
 // One workgroup of 64 threads per (query head, sequence).  Sequences with an
 // empty context get o = 0, lse = -inf; units cut by range boundaries get their
 // partials merged: (w0, slot 1) from the wave where the unit starts, then
-// (w, slot 0) for the following waves up to the one where it ends.
-template <typename TT>
+// (w, slot 0) for the following waves up to the one where it ends.  Lane k
+// reads the (m, l) of partial k; the weights 2^(m_k - M) are then broadcast
+// and the O rows of eight partials are loaded at once, so the whole merge
+// costs a few dependent memory round trips whatever the number of partials.
+template <typename TT, int D>
 __global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p, int W) {
   typedef typename TT::elem T;
+  constexpr int CPL = D / 64;   // output columns per lane
   const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  const int D = p.head_dim;
   const int kvh = h / p.group, g = h - kvh * p.group;
   T* og = (T*)p.o + ((int64_t)s * p.h_q + h) * D;
   const int nb = seq_blocks(p.context_lens[s]);
   if (nb == 0) {
-    for (int d = lane; d < D; d += 64) og[d] = (T)0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) og[lane * CPL + c] = (T)0.f;
     if (p.lse != nullptr && lane == 0) p.lse[(int64_t)s * p.h_q + h] = -INFINITY;
     return;
   }
@@ -392,29 +396,54 @@ __global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p
   auto slot_of = [&](int k) -> int64_t {
     return k == 0 ? ((int64_t)w0 * 2 + 1) * p.group + g : ((int64_t)(w0 + k) * 2) * p.group + g;
   };
-  float M = -INFINITY;
-  for (int k = lane; k < np; k += 64)
-    if (has_part(k)) M = fmaxf(M, p.ws_ml[slot_of(k) * 2]);
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
-  float L = 0.f;
+  // pass 1: per-lane online merge of (m, l) over partials lane, lane + 64, ...
+  float ml = -INFINITY, ll = 0.f;
   for (int k = lane; k < np; k += 64) {
     if (!has_part(k)) continue;
-    const int64_t sl = slot_of(k);
-    L += fast_exp2(p.ws_ml[sl * 2] - M) * p.ws_ml[sl * 2 + 1];
+    const float2 v = *(const float2*)(p.ws_ml + slot_of(k) * 2);
+    const float mn = fmaxf(ml, v.x);
+    ll = ll * fast_exp2(ml - mn) + v.y * fast_exp2(v.x - mn);
+    ml = mn;
   }
+  float M = ml;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+  float L = ml == -INFINITY ? 0.f : ll * fast_exp2(ml - M);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) L += __shfl_xor(L, sh);
   const float inv = 1.f / L;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int k = 0; k < np; ++k) {
-      if (!has_part(k)) continue;
-      const int64_t sl = slot_of(k);
-      acc += fast_exp2(p.ws_ml[sl * 2] - M) * p.ws_o[sl * D + d];
+  // pass 2: O = sum_k 2^(m_k - M) O_k / L, eight partials per round trip
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int c0 = 0; c0 < np; c0 += 64) {
+    const int k = c0 + lane;
+    float wl = 0.f;   // 0 marks "no partial": such slots are skipped, not scaled
+    if (k < np && has_part(k)) wl = fast_exp2(p.ws_ml[slot_of(k) * 2] - M);
+    const int n = np - c0 < 64 ? np - c0 : 64;
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float wk[8], v[8][CPL];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = j0 + j < n ? j0 + j : n - 1;   // clamped: always a valid slot
+        wk[j] = j0 + j < n ? __shfl(wl, kk) : 0.f;
+        const float* src = p.ws_o + slot_of(c0 + kk) * D + lane * CPL;
+        if constexpr (CPL == 2) {
+          const float2 t = *(const float2*)src;
+          v[j][0] = t.x;
+          v[j][1] = t.y;
+        } else {
+          v[j][0] = src[0];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += wk[j] != 0.f ? wk[j] * v[j][c] : 0.f;
     }
-    og[d] = (T)(acc * inv);
   }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) og[lane * CPL + c] = (T)(acc[c] * inv);
   if (p.lse != nullptr && lane == 0) p.lse[(int64_t)s * p.h_q + h] = (M + __log2f(L)) * kLn2;
 }
 
@@ -439,7 +468,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, int W, hipStream_t stre
   hipLaunchKernelGGL((paged_decode_split_kernel<TT, D, GP, RING>), dim3(W), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((paged_decode_combine_kernel<TT>), dim3(p.h_q, p.num_seqs), dim3(64), 0,
+  hipLaunchKernelGGL((paged_decode_combine_kernel<TT, D>), dim3(p.h_q, p.num_seqs), dim3(64), 0,
                      stream, p, W);
   return hipGetLastError();
 }

@@ -66,19 +66,26 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   constexpr int NS = D / 16;              // k-steps of one S^T half (8 for d = 128)
   constexpr int NQK = 2 * NS;             // QK matrix ops per tile
   constexpr int NPV = (D / 32) * (BN / 16);  // PV matrix ops per tile
-  // The running max is only raised when a row's maximum exceeds it by more
-  // than TAU (log2 units); until then probabilities are taken relative to the
-  // stale max and stay below 2^TAU.  The final division by l uses the same
-  // reference, so the result is unchanged; the O rescale is skipped whenever
-  // no row of the wave moved.
-  constexpr float TAU = 8.0f;
+  // Probabilities are taken relative to a per-row reference m that moves
+  // only when it has to (the division by l in the epilogue uses the same
+  // reference, so the result does not depend on it): when a row's maximum
+  // exceeds m by more than GROW (log2 units), m is set to that maximum plus
+  // HEAD and O and l are rescaled; until then every probability stays below
+  // 2^GROW.  For bf16 (fp32 exponent range) the headroom lets the maximum
+  // rise by HEAD + GROW before the next rescale: probabilities are at most
+  // 2^-HEAD relative to m's maximum, and terms more than HEAD + 66 below the
+  // row maximum, which flush to zero, weigh less than 2^-52 in total.  fp16
+  // probabilities must stay in fp16 range, so there m is the maximum itself.
+  constexpr float HEAD = TT::kIsBf16 ? 60.f : 0.f;
+  constexpr float GROW = TT::kIsBf16 ? 40.f : 8.f;
   static_assert(LOADS * 256 == BN * CPR, "tile split");
   static_assert(32 % (NQK + NPV) == 0, "slot plan");
   __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31;   // query column of this lane
   const int hi = lane >> 5;    // which half of the k slots / key rows
 
@@ -253,12 +260,13 @@ void attn_fwd_mfma_kernel(FwdParams p) {
           }
       }
       const float tmax = pair_max32(smax_cur) * c;
-      const bool grow = tmax > m_run + TAU;
+      const bool grow = tmax > m_run + GROW;
       // lanes that do not grow keep their reference (alpha = 1, which also
       // covers rows that have not seen a visible key, m = -inf); a row
       // leaving -inf gets alpha = 0
-      const float alpha = fast_exp2(grow ? m_run - tmax : 0.f);
-      m_run = grow ? tmax : m_run;
+      const float m_new = tmax + HEAD;
+      const float alpha = fast_exp2(grow ? m_run - m_new : 0.f);
+      m_run = grow ? m_new : m_run;
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
       // ---- 32 slots: one matrix op each (S_{kt+1} then O += P_{kt-1}
