@@ -35,7 +35,7 @@
 namespace attn {
 
 constexpr int kDecBS = 16;          // tokens per KV block
-constexpr int kDecMaxWaves = 2048;  // persistent waves (8 per CU on 256 CUs)
+constexpr int kDecMaxWaves = 2048;  // persistent waves: 8 per CU on 256 CUs (2 per SIMD)
 
 // Blocks of a sequence (one unit per KV head).
 __device__ inline int seq_blocks(int ctx) { return ctx > 0 ? (ctx + kDecBS - 1) / kDecBS : 0; }
@@ -51,8 +51,16 @@ __device__ inline int wave_of(int64_t b, int64_t T, int W) {
   return w;
 }
 
+// Read-only metadata (context lengths, block table) is read through the
+// constant address space: at a wave-uniform index that is a scalar load, which
+// keeps the cursor in scalar registers and lets the vector-memory counter track
+// K/V loads only.
+__device__ inline int ld_meta(const int32_t* ptr, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
+}
+
 // Total blocks over all sequences and the blocks of sequences before `s`,
-// reduced across the 64 lanes of the calling wave.
+// reduced across the 64 lanes of the calling wave (the results are uniform).
 __device__ inline void seq_block_sums(const DecodeParams& p, int s, int lane, int64_t& before,
                                       int64_t& total) {
   before = 0;
@@ -66,13 +74,17 @@ __device__ inline void seq_block_sums(const DecodeParams& p, int s, int lane, in
       a += __shfl_xor(a, sh);
       t += __shfl_xor(t, sh);
     }
-    before += a;
-    total += t;
+    before += __builtin_amdgcn_readfirstlane(a);
+    total += __builtin_amdgcn_readfirstlane(t);
   }
 }
 
 template <typename TT, int D, int GP, int RING>
-__global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) {
+// Two waves per SIMD (8 per CU) while the output partials (GP heads x D
+// columns) are small enough, one for larger ones, which need the registers.
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
+                          amdgpu_waves_per_eu(GP * D <= 512 ? 2 : 1, GP * D <= 512 ? 2 : 1)))
+void paged_decode_split_kernel(DecodeParams p) {
   typedef typename TT::elem T;
   constexpr int KST = D / 32;            // k-steps of q.K^T (16x16x32)
   constexpr int CH = D / 8;              // 16-byte chunks per K/V row
@@ -106,24 +118,41 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
     int64_t ustart;
     int lb;
   };
+  // list position b -> cursor: the sequences' list spans are prefix-summed
+  // across the wave, 64 sequences per round of loads, and the lane whose span
+  // holds b is picked by a ballot
   auto seek = [&](int64_t b) {
     Cursor cu{};
-    int64_t pos = 0;
-    for (int s = 0;; ++s) {
-      const int ctx = p.context_lens[s];
-      const int nb = seq_blocks(ctx);
-      const int64_t span = (int64_t)nb * p.h_kv;
-      if (b < pos + span) {
-        cu.s = s;
-        cu.kvh = (int)((b - pos) / nb);
-        cu.nblk = nb;
-        cu.ctx = ctx;
-        cu.ustart = pos + (int64_t)cu.kvh * nb;
+    int64_t base = 0;
+    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+      const int ss = s0 + lane;
+      const int ctx = ss < p.num_seqs ? p.context_lens[ss] : 0;
+      const int64_t span = (int64_t)seq_blocks(ctx) * p.h_kv;
+      int64_t incl = span;
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const int64_t t = __shfl_up(incl, sh);
+        if (lane >= sh) incl += t;
+      }
+      const int64_t lo = base + incl - span;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(span > 0 && b >= lo && b < lo + span);
+      if (hit != 0) {
+        const int l = (int)__builtin_ctzll(hit);
+        cu.s = s0 + l;
+        cu.ctx = __builtin_amdgcn_readlane(ctx, l);
+        cu.nblk = seq_blocks(cu.ctx);
+        const int64_t pos = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(lo >> 32), l) << 32) |
+                                      (uint32_t)__builtin_amdgcn_readlane((int)lo, l));
+        cu.kvh = (int)((b - pos) / cu.nblk);
+        cu.ustart = pos + (int64_t)cu.kvh * cu.nblk;
         cu.lb = (int)(b - cu.ustart);
         return cu;
       }
-      pos += span;
+      const int64_t tot = __shfl(incl, 63);
+      base += (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tot >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)tot));
     }
+    return cu;   // not reached: b lies inside the list
   };
   auto advance = [&](Cursor& cu) {
     if (++cu.lb < cu.nblk) return;
@@ -133,7 +162,7 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
     cu.kvh = 0;
     do {   // next sequence with blocks (past the end: a harmless dummy unit)
       ++cu.s;
-      cu.ctx = (cu.s < p.num_seqs) ? p.context_lens[cu.s] : 1;
+      cu.ctx = (cu.s < p.num_seqs) ? ld_meta(p.context_lens, cu.s) : 1;
       cu.nblk = seq_blocks(cu.ctx);
     } while (cu.nblk == 0);
   };
@@ -153,15 +182,25 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
   const uint32_t vl = (uint32_t)(2 * vrow * D + (lane % CH) * 8) * 2u;
 
   u32x4 kr[RING][KST], vr[RING][VST];
-  auto issue = [&](const Cursor& cu, int slot) {
-    const int64_t phys = p.block_table[(int64_t)cu.s * p.max_blocks_per_seq + cu.lb];
-    const char* kb = kc + (phys * p.h_kv + cu.kvh) * blk_bytes + kl;
-    const char* vb = vc + (phys * p.h_kv + cu.kvh) * blk_bytes + vl;
+  // Loads of one (block, KV head) tile through buffer resources based at the
+  // tile (scalar base, every lane offset inside it).  A refill past the end of
+  // the range uses an empty resource: the loads still issue, in the same
+  // order, but return zeros without touching memory.
+  auto issue = [&](const Cursor& cu, int slot, bool real) {
+    const char* kb = kc;
+    const char* vb = vc;
+    if (real) {
+      const int64_t phys = ld_meta(p.block_table, (int64_t)cu.s * p.max_blocks_per_seq + cu.lb);
+      kb += (phys * p.h_kv + cu.kvh) * blk_bytes;
+      vb += (phys * p.h_kv + cu.kvh) * blk_bytes;
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, real ? (uint32_t)blk_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, real ? (uint32_t)blk_bytes : 0u);
 #pragma unroll
-    for (int st = 0; st < KST; ++st) kr[slot][st] = *(const u32x4*)(kb + st * 64);
+    for (int st = 0; st < KST; ++st) kr[slot][st] = buf_load16(rk, kl + st * 64);
 #pragma unroll
     for (int st = 0; st < VST; ++st)
-      vr[slot][st] = *(const u32x4*)(vb + ((st & 1) + (st >> 1) * 2 * ROWS) * D * 2);
+      vr[slot][st] = buf_load16(rv, vl + ((st & 1) + (st >> 1) * 2 * ROWS) * D * 2);
   };
   // query heads of a unit as the A operand of S = Q K^T (rows = heads, zero padded)
   u32x4 qa[KST];
@@ -174,6 +213,10 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
       qa[st] = u32x4{0, 0, 0, 0};
       if (g < group) qa[st] = *(const u32x4*)(qg + 32 * st);
     }
+    // Drain here, once per unit (vmcnt(0); expcnt and lgkmcnt unconstrained).
+    // The Q loads are issued after the K/V loads in flight; waiting for them
+    // at each block would drain the whole ring every block.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   };
 
   // running state of the current unit: reference max of the heads of this
@@ -326,39 +369,45 @@ __global__ __launch_bounds__(64) void paged_decode_split_kernel(DecodeParams p) 
   Cursor pcur = icur;       // next block to process
 #pragma unroll
   for (int j = 0; j < RING; ++j) {
-    if (j < n) {
-      issue(icur, j);
-      advance(icur);
-    }
+    issue(icur, j, j < n);
+    if (j < n) advance(icur);
   }
   load_q(pcur);
   reset();
   int64_t seg_start = b0;
-  for (int i = 0; i < n; i += RING) {
-#pragma unroll
-    for (int j = 0; j < RING; ++j) {
-      const int k = i + j;
-      if (k < n) {
-        process(pcur, j);
-        if (k + RING < n) {
-          issue(icur, j);
-          advance(icur);
-        }
-        if (pcur.lb == pcur.nblk - 1 || k == n - 1) {
-          // the unit, or this wave's range, ends with this block
-          finish(pcur, seg_start, b0 + k + 1);
-          if (k + 1 < n) {
-            advance(pcur);
-            seg_start = b0 + k + 1;
-            load_q(pcur);
-            reset();
-          }
-        } else {
-          advance(pcur);
-        }
-      }
+  // one block: process it, refill its ring slot with the block RING ahead,
+  // and close the unit (or this wave's range) when it ends here
+  auto step = [&](int k, int j, bool refill) {
+    process(pcur, j);
+    if (refill) {
+      const bool real = k + RING < n;
+      issue(icur, j, real);
+      if (real) advance(icur);
     }
+    if (pcur.lb == pcur.nblk - 1 || k == n - 1) {
+      finish(pcur, seg_start, b0 + k + 1);
+      if (k + 1 < n) {
+        advance(pcur);
+        seg_start = b0 + k + 1;
+        load_q(pcur);
+        reset();
+      }
+    } else {
+      advance(pcur);
+    }
+  };
+  // steady state: every slot is refilled (with an empty load past the end),
+  // so the loads are always issued in the same order and each block waits
+  // only for its own loads
+  int i = 0;
+  for (; i + RING <= n; i += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) step(i + j, j, true);
   }
+  // the last (fewer than RING) blocks are already in the ring
+#pragma unroll
+  for (int t = 0; t < RING - 1; ++t)
+    if (i + t < n) step(i + t, t, false);
 }
 
 // One workgroup of 64 threads per (query head, sequence).  Sequences with an
@@ -464,7 +513,10 @@ size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int
 
 template <typename TT, int D, int GP>
 static hipError_t launch_decode_t(const DecodeParams& p, int W, hipStream_t stream) {
-  constexpr int RING = GP <= 4 ? 3 : 2;
+  constexpr int RING = 2;
+  // as many waves as are resident at once (one per SIMD when GP x D > 512),
+  // so that no wave waits for another to finish before it starts
+  if (GP * D > 512 && W > kDecMaxWaves / 2) W = kDecMaxWaves / 2;
   hipLaunchKernelGGL((paged_decode_split_kernel<TT, D, GP, RING>), dim3(W), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

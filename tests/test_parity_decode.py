@@ -128,3 +128,33 @@ def test_deterministic(config4):
     out1, lse1 = _run(config4)
     out2, lse2 = _run(config4)
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def _long_case(h_q, h_kv, ctx_lo, ctx_hi, seed):
+    # long contexts: every (sequence, KV head) is cut across several waves
+    rng = np.random.default_rng(seed)
+    ctx = [int(c) for c in rng.integers(ctx_lo, ctx_hi, 8, endpoint=True)]
+    return workloads.decode_inputs(ctx, h_q=h_q, h_kv=h_kv, d=128, block_size=16,
+                                   dtype="bf16", seed=seed)
+
+
+def test_workspace_reused_with_garbage_contents():
+    # the workspace contents on entry do not matter: a caller-provided buffer
+    # filled with NaN bytes, reused for two calls, gives identical results
+    inp = _long_case(32, 8, 2048, 2300, 60)
+    mcl = int(inp.context_lens.max())
+    need = ea.paged_attn_decode_workspace_size(8, 32, 8, 128, mcl)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    out1, lse1 = _run(inp, workspace=ws)
+    out2, lse2 = _run(inp, workspace=ws)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    ref, ref_lse = _oracle(inp)
+    assert_close(out1, ref, torch.bfloat16, "long contexts, reused workspace")
+    assert_lse_close(lse1, ref_lse, torch.bfloat16)
+
+
+@pytest.mark.parametrize("group,h_kv,lo,hi", [(8, 4, 2560, 2800), (16, 2, 4800, 5200)])
+def test_long_contexts_large_groups(group, h_kv, lo, hi):
+    # groups of 8 and 16 query heads at d = 128 run one wave per SIMD
+    inp = _long_case(group * h_kv, h_kv, lo, hi, 61 + group)
+    _check(inp, "long contexts, group %d" % group)
