@@ -90,6 +90,8 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
     // (batch, kv head) slice, including up to one tile past its end
     if (((int64_t)n_k + 128) * std::max(k_stride[1], v_stride[1]) * es >= ((int64_t)1 << 31))
       return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: one (batch, kv head) slice of k/v spans >= 2 GiB");
+    if (((int64_t)n_q + 128) * q_stride[1] * es >= ((int64_t)1 << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: one (batch, head) slice of q spans >= 2 GiB");
 
     attn::FwdParams p{};
     p.q = q;

@@ -174,6 +174,7 @@ struct FwdParams {
   int64_t os_b, os_n, os_h;
   int batch, n_q, n_k, h_q, h_kv, group;
   uint32_t k_bytes, v_bytes;  // byte extent of one (batch, kv head) slice of k / v
+  uint32_t q_bytes;           // byte extent of one (batch, head) slice of q
   int n_qtiles;     // ceil(n_q / BM)
   int num_items;    // n_qtiles * batch * h_q
   int xcd_chunk;    // work items kept together on one XCD (0 = no remap)

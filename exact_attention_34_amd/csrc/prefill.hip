@@ -112,14 +112,10 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
   const uint32_t krow = (uint32_t)p.ks_n * 2u, vrow = (uint32_t)p.vs_n * 2u;  // row pitch, bytes
 
-  // Q fragment (B operand of S^T = K Q^T): column = query, k = d.
+  // Q fragment (B operand of S^T = K Q^T): column = query, k = d.  Filled
+  // in the prologue through LDS (see below).
   const int qrow = q0 + wave * 32 + col;
   u32x4 qf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    qf[s] = u32x4{0, 0, 0, 0};
-    if (qrow < p.n_q) qf[s] = *(const u32x4*)(Qg + (int64_t)qrow * p.qs_n + 16 * s + hi * 8);
-  }
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -158,6 +154,22 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Kg + o, rem_b);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
+  };
+  // The Q tile (BM = 2 BN rows) goes through the V stages, which are idle
+  // until the first tile: two BN-row tiles in the K layout, loaded the same
+  // coalesced way (rows past n_q read as zero).
+  const uint32_t qrowb = (uint32_t)p.qs_n * 2u;
+  auto load_q = [&](int t) {
+    const uint32_t o = (uint32_t)(q0 + t * BN) * qrowb;
+    const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.q_bytes > o ? p.q_bytes - o : 0u);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Qg + o, rem_b);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot = (i * 4 + wave) * 64 + lane;
+      const int row = slot / CPR, pc = slot % CPR;
+      buf_load16_lds(r, vs_lds + t * TILE + (i * 4 + wave) * 512,
+                     (uint32_t)row * qrowb + (uint32_t)((pc ^ kswz(row)) * 16));
+    }
   };
   auto load_v = [&](int kt, int stage) {
     const uint32_t o = (uint32_t)(kt * BN) * vrow;
@@ -199,13 +211,23 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const int klast = CAUSAL ? min(qrow + off, p.n_k - 1) : p.n_k - 1;
 
   if (ntiles > 0) {
-    // ---- prologue: K_0 and K_1 staged, the "previous" V stage zeroed, S_0 ----
+    // ---- prologue: Q through LDS, K_0 and K_1 staged, the "previous" V
+    // stage zeroed, S_0 ----
+    load_q(0);
+    load_q(1);
     load_k(0, 0);
     load_k(1, 1);
+    wait_loads_and_sync();
+    {
+      // this wave's 32 rows sit in Q tile wave / 2, rows 32 (wave % 2) + ...
+      const uint16_t* qb = vs_lds + (wave >> 1) * TILE + (wave & 1) * 32 * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qb + kofs[s]);
+    }
+    __syncthreads();   // every wave holds its Q fragment before the V stages are reused
 #pragma unroll
     for (int i = 0; i < TILE / 8 / 256; ++i)
       *(u32x4*)(vs_lds + TILE + (tid + 256 * i) * 8) = u32x4{0, 0, 0, 0};
-    wait_loads_and_sync();
     f32x16 st_cur[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -496,6 +518,7 @@ static hipError_t launch_mfma(FwdParams p, hipStream_t stream) {
   // bytes from the first row of a (batch, kv head) slice to the end of its last row
   p.k_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.ks_n + D) * 2) : 0u;
   p.v_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.vs_n + D) * 2) : 0u;
+  p.q_bytes = p.n_q > 0 ? (uint32_t)(((int64_t)(p.n_q - 1) * p.qs_n + D) * 2) : 0u;
   hipLaunchKernelGGL((attn_fwd_mfma_kernel<TT, D, CAUSAL>), dim3(p.num_items), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
