@@ -404,8 +404,14 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   // ---- epilogue: O = O^T / l, LSE ----
   const float l_tot = pair_sum32(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (qrow < p.n_q) {
-    T* Og = (T*)p.o + (int64_t)b * p.os_b + (int64_t)qrow * p.os_n + (int64_t)h * p.os_h;
+  {
+    // Each wave's 32 output rows go through LDS (rows padded by 16 bytes
+    // against bank conflicts) so that each store instruction writes four
+    // whole rows instead of 8-byte pieces of 32 rows.
+    constexpr int OP = D + 8;   // padded row, elements
+    static_assert(4 * 32 * OP <= 4 * TILE, "O staging fits the K and V stages");
+    __syncthreads();            // every wave is done with the K/V stages
+    uint16_t* ow = (wave < 2 ? ks_lds : vs_lds) + (wave & 1) * 32 * OP;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -413,8 +419,21 @@ void attn_fwd_mfma_kernel(FwdParams p) {
         u32x2 w;
         w.x = TT::pack2(oacc[t][4 * g + 0] * inv, oacc[t][4 * g + 1] * inv);
         w.y = TT::pack2(oacc[t][4 * g + 2] * inv, oacc[t][4 * g + 3] * inv);
-        *(u32x2*)(Og + t * 32 + g * 8 + hi * 4) = w;
+        *(u32x2*)(ow + col * OP + t * 32 + g * 8 + hi * 4) = w;
       }
+    lds_order();
+    // lane l: chunk l % CPR of row (l / CPR) + (64 / CPR) i of this wave's rows
+    constexpr int RPI = 64 / CPR;   // rows per store instruction
+    T* Ob = (T*)p.o + (int64_t)b * p.os_b + (int64_t)h * p.os_h;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / CPR;
+      const int grow = q0 + wave * 32 + r;
+      const u32x4 v = *(const u32x4*)(ow + r * OP + (lane % CPR) * 8);
+      if (grow < p.n_q) *(u32x4*)(Ob + (int64_t)grow * p.os_n + (lane % CPR) * 8) = v;
+    }
+  }
+  if (qrow < p.n_q) {
     if (p.lse != nullptr && hi == 0) {
       p.lse[((int64_t)b * p.h_q + h) * p.n_q + qrow] =
           (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
