@@ -16,6 +16,9 @@ Kernel times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB copies, for counters
+    python bench.py --write-traffic FETCH WRITE COPY_FETCH COPY_WRITE
+        # profiles/traffic.json from four rocprofv3 --pmc output directories:
+        # FETCH_SIZE and WRITE_SIZE of a bench run, then of --copy-calibration
 """
 
 import argparse
@@ -70,7 +73,59 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one kernel family only (for profiling)")
+    ap.add_argument("--write-traffic", nargs=4, default=None,
+                    metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     return ap.parse_args()
+
+
+TRAFFIC_KERNELS = {   # entry name -> kernel name prefix in rocprofv3 output
+    "attn_fwd_mfma_kernel": "void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true>",
+    "paged_decode_split_kernel": "void attn::paged_decode_split_kernel<attn::BF16, 128, 4,",
+    "paged_decode_combine_kernel": "void attn::paged_decode_combine_kernel<attn::BF16",
+}
+
+
+def _counter_kib(directory, counter, prefix):
+    """Mean KiB per dispatch of `counter` over the kernels whose name starts
+    with `prefix`, from rocprofv3 counter_collection.csv files."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(prefix):
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no %s samples for %s in %s" % (counter, prefix, directory))
+    return float(np.mean(vals)), len(vals)
+
+
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per launch: counter KiB scaled by what the same counter reads
+    for plain device copies of known size (bench.py --copy-calibration)."""
+    copy_bytes = 1 << 30
+    cf, _ = _counter_kib(copy_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    cw, _ = _counter_kib(copy_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    ff, wf = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    out = {
+        "_about": "HBM bytes per launch of each kernel on the benchmark workloads, from "
+                  "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch) scaled by "
+                  "the reading of the same counters for a plain 1 GiB device copy (fetch factor "
+                  "%.4f, write factor %.4f). Valid only while the kernel sources hash to "
+                  "source_hash." % (ff, wf),
+        "fetch_factor": ff, "write_factor": wf,
+    }
+    for name, prefix in TRAFFIC_KERNELS.items():
+        fk, n1 = _counter_kib(fetch_dir, "FETCH_SIZE", prefix)
+        wk, n2 = _counter_kib(write_dir, "WRITE_SIZE", prefix)
+        fb, wb = int(round(fk * 1024 * ff)), int(round(wk * 1024 * wf))
+        out[name] = {"kernel_prefix": prefix, "source_hash": source_hash(),
+                     "fetch_kib_raw": fk, "write_kib_raw": wk, "dispatches": [n1, n2],
+                     "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def copy_calibration():
@@ -124,6 +179,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
         return
     import exact_attention_34_amd as ea
     import workloads
