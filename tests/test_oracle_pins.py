@@ -18,6 +18,8 @@ import math
 import os
 
 import mpmath
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -88,7 +90,7 @@ BRUTE_CASES = [
 @pytest.mark.parametrize("case", BRUTE_CASES)
 def test_oracle_matches_brute_force(case):
     B, Nq, Nk, Hq, Hkv, d, causal = case
-    rng = np.random.default_rng(hash(case) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     q, k, v = _rand((B, Nq, Hq, d), rng), _rand((B, Nk, Hkv, d), rng), _rand((B, Nk, Hkv, d), rng)
     scale = 1.0 / math.sqrt(d)
     o, lse = oracle.sdpa(q, k, v, scale, causal)

@@ -8,6 +8,8 @@ properties that hold at any size.
 
 import math
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -111,7 +113,7 @@ SHAPES = [
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_shapes(shape):
     B, Nq, Nk, Hq, Hkv, d, dt, causal = shape
-    inp = workloads.prefill_inputs(B, Nq, Nk, Hq, Hkv, d, dt, seed=hash(shape) % 2**31,
+    inp = workloads.prefill_inputs(B, Nq, Nk, Hq, Hkv, d, dt, seed=zlib.crc32(repr(shape).encode()),
                                    causal=causal)
     _check_full(inp, "shape %s" % (shape,))
 
