@@ -66,6 +66,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   constexpr int NS = D / 16;              // k-steps of one S^T half (8 for d = 128)
   constexpr int NQK = 2 * NS;             // QK matrix ops per tile
   constexpr int NPV = (D / 32) * (BN / 16);  // PV matrix ops per tile
+  constexpr int PFD = 3;                  // LDS operand prefetch distance, in slots
   // Probabilities are taken relative to a per-row reference m that moves
   // only when it has to (the division by l in the epilogue uses the same
   // reference, so the result does not depend on it): when a row's maximum
@@ -292,7 +293,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
       // ---- 32 slots: one matrix op each (S_{kt+1} then O += P_{kt-1}
-      // V_{kt-1}), its LDS operand fetched two slots ahead, and a few vector
+      // V_{kt-1}), its LDS operand fetched PFD slots ahead, and a few vector
       // ops of the softmax of S_kt / the row max of S_{kt+1} ----
       const uint16_t* kb = ks_lds + S * TILE;
       const uint16_t* vb = vs_lds + S * TILE;
@@ -311,12 +312,11 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       u32x4 pb_cur[4];
       float psum = 0.f, pe_prev = 0.f, smax_next = -INFINITY;
       u32x4 opnd[NSLOT];
-      opnd[0] = fetch(0);
-      opnd[1] = fetch(1);
-      opnd[2] = fetch(2);
+#pragma unroll
+      for (int i = 0; i < PFD; ++i) opnd[i] = fetch(i);
 #pragma unroll
       for (int i = 0; i < NSLOT; ++i) {
-        if (i + 3 < NSLOT) opnd[i + 3] = fetch(i + 3);
+        if (i + PFD < NSLOT) opnd[i + PFD] = fetch(i + PFD);
         if (i < NQK) {
           const int sub = i / NS, s = i % NS;
           if (s == 0) {
