@@ -19,7 +19,8 @@ from . import build as _build
 
 __all__ = [
     "AttnError", "lib", "abi_version", "attn_fwd", "paged_attn_decode",
-    "paged_attn_decode_workspace_size", "LIB_PATH",
+    "paged_attn_decode_workspace_size", "paged_attn_decode_shared",
+    "paged_attn_decode_shared_workspace_size", "LIB_PATH",
 ]
 
 LIB_PATH = _build.LIB_PATH
@@ -67,6 +68,12 @@ def lib():
     L.paged_attn_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, ctypes.c_size_t, vp]
+    L.paged_attn_decode_shared_workspace_size.restype = ctypes.c_size_t
+    L.paged_attn_decode_shared_workspace_size.argtypes = [i32] * 8
+    L.paged_attn_decode_shared.restype = i32
+    L.paged_attn_decode_shared.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                           i32, f32, vp, ctypes.c_size_t, vp]
     _LIB = L
     return L
 
@@ -143,17 +150,8 @@ def paged_attn_decode_workspace_size(num_seqs, h_q, h_kv, head_dim, max_context_
                                                        max_context_len))
 
 
-def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len,
-                      scale=None, out=None, lse=None, workspace=None, return_lse=False):
-    """Single-token decode over a paged KV cache.
-
-    ``q``: ``[S][Hq][d]``; ``k_cache``, ``v_cache``:
-    ``[num_blocks][Hkv][16][d]`` (contiguous, float16 or bfloat16);
-    ``block_table``: ``[S][max_blocks_per_seq]`` int32; ``context_lens``:
-    ``[S]`` int32, each at most ``max_context_len`` (a host int).  The
-    workspace is allocated from torch's caching allocator when not given.
-    Asynchronous on the current stream.
-    """
+def _decode_common(q, k_cache, v_cache, block_table, context_lens, scale, out, lse,
+                   return_lse):
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("q must be [S][Hq][d] and the caches [blocks][Hkv][bs][d]")
     if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype \
@@ -167,8 +165,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_contex
         if not t.is_cuda or t.device != q.device:
             raise ValueError("all tensors must be on the same GPU")
     S, Hq, d = q.shape
-    NB, Hkv, bs, dk = k_cache.shape
-    if dk != d:
+    if k_cache.shape[3] != d:
         raise ValueError("head_dim mismatch")
     if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_table must be [S][max_blocks] and context_lens [S]")
@@ -183,6 +180,24 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_contex
     if lse is not None and (lse.shape != (S, Hq) or lse.dtype != torch.float32
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [S][Hq] tensor")
+    return scale, out, lse
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                      scale=None, out=None, lse=None, workspace=None, return_lse=False):
+    """Single-token decode over a paged KV cache.
+
+    ``q``: ``[S][Hq][d]``; ``k_cache``, ``v_cache``:
+    ``[num_blocks][Hkv][16][d]`` (contiguous, float16 or bfloat16);
+    ``block_table``: ``[S][max_blocks_per_seq]`` int32; ``context_lens``:
+    ``[S]`` int32, each at most ``max_context_len`` (a host int).  The
+    workspace is allocated from torch's caching allocator when not given.
+    Asynchronous on the current stream.
+    """
+    scale, out, lse = _decode_common(q, k_cache, v_cache, block_table, context_lens, scale,
+                                     out, lse, return_lse)
+    S, Hq, d = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
     need = paged_attn_decode_workspace_size(S, Hq, Hkv, d, int(max_context_len))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -192,6 +207,55 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_contex
                                    S, Hq, Hkv, d, bs, block_table.shape[1], int(max_context_len),
                                    NB, float(scale), _ptr(workspace), ws_bytes,
                                    _stream(q.device))
+    _check(code)
+    if return_lse:
+        return out, lse
+    return out
+
+
+def paged_attn_decode_shared_workspace_size(num_seqs, num_groups, max_group_size, h_q, h_kv,
+                                            head_dim, max_context_len, max_prefix_len):
+    """Bytes of workspace :func:`paged_attn_decode_shared` needs (0 if invalid)."""
+    return int(lib().paged_attn_decode_shared_workspace_size(
+        num_seqs, num_groups, max_group_size, h_q, h_kv, head_dim, max_context_len,
+        max_prefix_len))
+
+
+def paged_attn_decode_shared(q, k_cache, v_cache, block_table, context_lens, group_starts,
+                             prefix_lens, max_context_len, max_group_size, max_prefix_len,
+                             scale=None, out=None, lse=None, workspace=None,
+                             return_lse=False):
+    """Single-token decode for groups of sequences that share a prefix.
+
+    Arguments as :func:`paged_attn_decode`, plus ``group_starts``
+    (``[G + 1]`` int32 on the GPU: group ``g`` is sequences
+    ``group_starts[g] .. group_starts[g+1]-1``) and ``prefix_lens`` (``[G]``
+    int32 on the GPU: tokens of each group's common prefix, whose block ids
+    are the same in every member's table row), with host-side bounds
+    ``max_group_size`` and ``max_prefix_len``.  Each shared prefix block is
+    read once per group.  Asynchronous on the current stream.
+    """
+    scale, out, lse = _decode_common(q, k_cache, v_cache, block_table, context_lens, scale,
+                                     out, lse, return_lse)
+    for t in (group_starts, prefix_lens):
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda \
+                or t.device != q.device:
+            raise ValueError("group_starts and prefix_lens must be contiguous int32 GPU tensors")
+    G = prefix_lens.shape[0]
+    if group_starts.shape != (G + 1,):
+        raise ValueError("group_starts must have one more entry than prefix_lens")
+    S, Hq, d = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    need = paged_attn_decode_shared_workspace_size(S, G, int(max_group_size), Hq, Hkv, d,
+                                                   int(max_context_len), int(max_prefix_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = lib().paged_attn_decode_shared(
+        _DTYPE_CODE[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(context_lens), _ptr(group_starts), _ptr(prefix_lens), _ptr(out), _ptr(lse),
+        S, G, int(max_group_size), Hq, Hkv, d, bs, block_table.shape[1], int(max_context_len),
+        int(max_prefix_len), NB, float(scale), _ptr(workspace), ws_bytes, _stream(q.device))
     _check(code)
     if return_lse:
         return out, lse

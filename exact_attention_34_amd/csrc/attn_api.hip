@@ -13,8 +13,11 @@ namespace attn {
 hipError_t launch_prefill(int dtype, int head_dim, bool causal, const FwdParams& p,
                           hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeParams& p, int max_context_len, hipStream_t stream);
+hipError_t launch_decode_shared(int dtype, const DecodeParams& p, int64_t items,
+                                int max_context_len, hipStream_t stream);
 size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int max_context_len);
 int decode_waves(int num_seqs, int h_kv, int max_context_len);
+SharedPlan shared_plan(int num_groups, int max_group_size, int h_q, int h_kv, int max_prefix_len);
 }  // namespace attn
 
 namespace {
@@ -29,6 +32,99 @@ int fail(int code, const std::string& msg) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 int elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Byte offsets of the regions of the shared-prefix decode workspace: the
+// split kernel's partials first (as in plain decode), then the per-(sequence,
+// head) suffix results, the prefix partials and the per-sequence metadata.
+struct SharedWs {
+  size_t suf_o, suf_ml, pre_o, pre_ml, meta, total;
+};
+SharedWs shared_ws(int num_seqs, int h_q, int head_dim, size_t split_bytes, int64_t items) {
+  SharedWs w{};
+  size_t off = align16(split_bytes);
+  w.suf_o = off;
+  off = align16(off + (size_t)num_seqs * h_q * head_dim * 4);
+  w.suf_ml = off;
+  off = align16(off + (size_t)num_seqs * h_q * 2 * 4);
+  w.pre_o = off;
+  off = align16(off + (size_t)items * 32 * head_dim * 4);
+  w.pre_ml = off;
+  off = align16(off + (size_t)items * 32 * 2 * 4);
+  w.meta = off;
+  off = align16(off + (size_t)num_seqs * 3 * 4);
+  w.total = off;
+  return w;
+}
+
+// Checks common to both decode entry points (everything but the workspace);
+// on success fills the fields of p that plain decode uses.
+int check_decode(const char* fn, int dtype, const void* q, const void* k_cache,
+                 const void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                 void* o, float* lse, int num_seqs, int h_q, int h_kv, int head_dim,
+                 int block_size, int max_blocks_per_seq, int max_context_len, int num_blocks,
+                 float softmax_scale, attn::DecodeParams& p) {
+  const std::string f(fn);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, f + ": dtype must be ATTN_F16 or ATTN_BF16");
+  if (num_seqs < 0 || h_q < 0 || h_kv < 0 || head_dim < 0 || block_size < 0 ||
+      max_blocks_per_seq < 0 || max_context_len < 0 || num_blocks < 0)
+    return fail(ATTN_ERR_SHAPE, f + ": sizes must be non-negative");
+  if (h_kv == 0 || h_q == 0 || (h_q % h_kv) != 0)
+    return fail(ATTN_ERR_SHAPE, f + ": h_q must be a positive multiple of h_kv");
+  if (h_q / h_kv > 16)
+    return fail(ATTN_ERR_UNSUPPORTED, f + ": at most 16 query heads per KV head");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, f + ": block_size must be 16");
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+    return fail(ATTN_ERR_SHAPE, f + ": softmax_scale must be finite and positive");
+  if ((int64_t)max_blocks_per_seq * block_size < (int64_t)max_context_len)
+    return fail(ATTN_ERR_SHAPE, f + ": max_blocks_per_seq * block_size < max_context_len");
+  if (max_context_len > 0 && num_blocks == 0)
+    return fail(ATTN_ERR_SHAPE, f + ": num_blocks must be positive");
+  if (num_seqs == 0) return ATTN_OK;
+  if (q == nullptr || o == nullptr || context_lens == nullptr)
+    return fail(ATTN_ERR_NULL, f + ": q, o and context_lens must not be NULL");
+  if (max_context_len > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
+    return fail(ATTN_ERR_NULL, f + ": k_cache, v_cache and block_table must not be NULL");
+  const void* ptrs[4] = {q, k_cache, v_cache, o};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr))
+      return fail(ATTN_ERR_ALIGN, f + ": q, caches and o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(context_lens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(ATTN_ERR_ALIGN, f + ": block_table, context_lens and lse must be 4-byte aligned");
+  if ((int64_t)num_seqs > 65535 || h_q > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, f + ": too many sequences or heads for one launch");
+  p = attn::DecodeParams{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.o = o;
+  p.lse = lse;
+  p.num_seqs = num_seqs;
+  p.h_q = h_q;
+  p.h_kv = h_kv;
+  p.group = h_q / h_kv;
+  p.head_dim = head_dim;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.scale_log2 = softmax_scale * attn::kLog2e;
+  return ATTN_OK;
+}
+
+int check_workspace(const char* fn, void* workspace, size_t workspace_bytes, size_t need) {
+  if (need == 0) return ATTN_OK;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, std::string(fn) + ": workspace of " + std::to_string(need) +
+                                        " bytes required, got " + std::to_string(workspace_bytes));
+  if (!aligned16(workspace))
+    return fail(ATTN_ERR_ALIGN, std::string(fn) + ": workspace must be 16-byte aligned");
+  return ATTN_OK;
+}
 
 bool debug_enabled() {
   static const bool on = [] {
@@ -138,70 +234,20 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
                       void* stream) {
   try {
     g_last_error.clear();
-    if (dtype != ATTN_F16 && dtype != ATTN_BF16)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: dtype must be ATTN_F16 or ATTN_BF16");
-    if (num_seqs < 0 || h_q < 0 || h_kv < 0 || head_dim < 0 || block_size < 0 ||
-        max_blocks_per_seq < 0 || max_context_len < 0 || num_blocks < 0)
-      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: sizes must be non-negative");
-    if (h_kv == 0 || h_q == 0 || (h_q % h_kv) != 0)
-      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: h_q must be a positive multiple of h_kv");
-    if (h_q / h_kv > 16)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: at most 16 query heads per KV head");
-    if (head_dim != 64 && head_dim != 128)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: head_dim must be 64 or 128");
-    if (block_size != 16)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: block_size must be 16");
-    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
-      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: softmax_scale must be finite and positive");
-    if ((int64_t)max_blocks_per_seq * block_size < (int64_t)max_context_len)
-      return fail(ATTN_ERR_SHAPE,
-                  "paged_attn_decode: max_blocks_per_seq * block_size < max_context_len");
-    if (max_context_len > 0 && num_blocks == 0)
-      return fail(ATTN_ERR_SHAPE, "paged_attn_decode: num_blocks must be positive");
-    if (num_seqs == 0) return ATTN_OK;
-    if (q == nullptr || o == nullptr || context_lens == nullptr)
-      return fail(ATTN_ERR_NULL, "paged_attn_decode: q, o and context_lens must not be NULL");
-    if (max_context_len > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
-      return fail(ATTN_ERR_NULL, "paged_attn_decode: k_cache, v_cache and block_table must not be NULL");
-    const void* ptrs[4] = {q, k_cache, v_cache, o};
-    for (const void* ptr : ptrs)
-      if (ptr != nullptr && !aligned16(ptr))
-        return fail(ATTN_ERR_ALIGN, "paged_attn_decode: q, caches and o must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
-        (reinterpret_cast<uintptr_t>(lse) & 3u))
-      return fail(ATTN_ERR_ALIGN, "paged_attn_decode: block_table, context_lens and lse must be 4-byte aligned");
+    attn::DecodeParams p;
+    int rc = check_decode("paged_attn_decode", dtype, q, k_cache, v_cache, block_table,
+                          context_lens, o, lse, num_seqs, h_q, h_kv, head_dim, block_size,
+                          max_blocks_per_seq, max_context_len, num_blocks, softmax_scale, p);
+    if (rc != ATTN_OK || num_seqs == 0) return rc;
     const size_t need = attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
-    if (need > 0) {
-      if (workspace == nullptr || workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE,
-                    "paged_attn_decode: workspace of " + std::to_string(need) + " bytes required, got " +
-                        std::to_string(workspace_bytes));
-      if (!aligned16(workspace))
-        return fail(ATTN_ERR_ALIGN, "paged_attn_decode: workspace must be 16-byte aligned");
-    }
-    if ((int64_t)num_seqs > 65535 || h_q > 65535)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged_attn_decode: too many sequences or heads for one launch");
-
-    attn::DecodeParams p{};
-    p.q = q;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.block_table = block_table;
-    p.context_lens = context_lens;
-    p.o = o;
-    p.lse = lse;
-    p.num_seqs = num_seqs;
-    p.h_q = h_q;
-    p.h_kv = h_kv;
-    p.group = h_q / h_kv;
-    p.head_dim = head_dim;
-    p.max_blocks_per_seq = max_blocks_per_seq;
-    p.scale_log2 = softmax_scale * attn::kLog2e;
+    rc = check_workspace("paged_attn_decode", workspace, workspace_bytes, need);
+    if (rc != ATTN_OK) return rc;
     if (need > 0) {
       const int64_t slots =
           (int64_t)attn::decode_waves(num_seqs, h_kv, max_context_len) * 2 * (h_q / h_kv);
       p.ws_o = static_cast<float*>(workspace);
       p.ws_ml = p.ws_o + slots * head_dim;
+      p.ws_unit = reinterpret_cast<int32_t*>(p.ws_ml + slots * 2);
     }
     if (debug_enabled())
       std::fprintf(stderr, "[attn] paged_attn_decode dtype=%d seqs=%d hq=%d hkv=%d d=%d waves=%d\n",
@@ -213,6 +259,91 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_ERR_HIP, "paged_attn_decode: unexpected host exception");
+  }
+}
+
+size_t paged_attn_decode_shared_workspace_size(int num_seqs, int num_groups, int max_group_size,
+                                               int h_q, int h_kv, int head_dim,
+                                               int max_context_len, int max_prefix_len) {
+  if (num_seqs <= 0 || num_groups <= 0 || max_group_size <= 0 || h_q <= 0 || h_kv <= 0 ||
+      head_dim <= 0 || max_context_len < 0 || max_prefix_len < 0 || h_q % h_kv != 0)
+    return 0;
+  const attn::SharedPlan pl =
+      attn::shared_plan(num_groups, max_group_size, h_q, h_kv, max_prefix_len);
+  const size_t split = attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
+  return shared_ws(num_seqs, h_q, head_dim, split, pl.items).total;
+}
+
+int paged_attn_decode_shared(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* context_lens,
+                             const int32_t* group_starts, const int32_t* prefix_lens, void* o,
+                             float* lse, int num_seqs, int num_groups, int max_group_size,
+                             int h_q, int h_kv, int head_dim, int block_size,
+                             int max_blocks_per_seq, int max_context_len, int max_prefix_len,
+                             int num_blocks, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "paged_attn_decode_shared";
+  try {
+    g_last_error.clear();
+    attn::DecodeParams p;
+    int rc = check_decode(fn, dtype, q, k_cache, v_cache, block_table, context_lens, o, lse,
+                          num_seqs, h_q, h_kv, head_dim, block_size, max_blocks_per_seq,
+                          max_context_len, num_blocks, softmax_scale, p);
+    if (rc != ATTN_OK) return rc;
+    if (num_groups < 0 || max_group_size < 0 || max_prefix_len < 0)
+      return fail(ATTN_ERR_SHAPE, std::string(fn) + ": sizes must be non-negative");
+    if (num_seqs == 0) return ATTN_OK;
+    if (num_groups == 0 || max_group_size == 0)
+      return fail(ATTN_ERR_SHAPE, std::string(fn) + ": every sequence must be in a group");
+    if (max_prefix_len > max_context_len)
+      return fail(ATTN_ERR_SHAPE, std::string(fn) + ": max_prefix_len > max_context_len");
+    if (group_starts == nullptr || prefix_lens == nullptr)
+      return fail(ATTN_ERR_NULL, std::string(fn) + ": group_starts and prefix_lens must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(group_starts) & 3u) || (reinterpret_cast<uintptr_t>(prefix_lens) & 3u))
+      return fail(ATTN_ERR_ALIGN, std::string(fn) + ": group_starts and prefix_lens must be 4-byte aligned");
+    const attn::SharedPlan pl =
+        attn::shared_plan(num_groups, max_group_size, h_q, h_kv, max_prefix_len);
+    if (pl.items >= ((int64_t)1 << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, std::string(fn) + ": problem too large for one launch");
+    const size_t split = attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
+    const SharedWs lay = shared_ws(num_seqs, h_q, head_dim, split, pl.items);
+    rc = check_workspace(fn, workspace, workspace_bytes, lay.total);
+    if (rc != ATTN_OK) return rc;
+    char* base = static_cast<char*>(workspace);
+    if (split > 0) {
+      const int64_t slots =
+          (int64_t)attn::decode_waves(num_seqs, h_kv, max_context_len) * 2 * (h_q / h_kv);
+      p.ws_o = reinterpret_cast<float*>(base);
+      p.ws_ml = p.ws_o + slots * head_dim;
+      p.ws_unit = reinterpret_cast<int32_t*>(p.ws_ml + slots * 2);
+    }
+    p.group_starts = group_starts;
+    p.prefix_lens = prefix_lens;
+    p.ws_suf_o = reinterpret_cast<float*>(base + lay.suf_o);
+    p.ws_suf_ml = reinterpret_cast<float*>(base + lay.suf_ml);
+    p.ws_pre_o = reinterpret_cast<float*>(base + lay.pre_o);
+    p.ws_pre_ml = reinterpret_cast<float*>(base + lay.pre_ml);
+    p.seq_meta = reinterpret_cast<int32_t*>(base + lay.meta);
+    p.first_block = p.seq_meta;
+    p.seq_group = p.seq_meta + num_seqs;
+    p.seq_member = p.seq_meta + 2 * num_seqs;
+    p.num_groups = num_groups;
+    p.n_rt = pl.n_rt;
+    p.n_ch = pl.n_ch;
+    p.chunk_blocks = pl.chunk_blocks;
+    if (debug_enabled())
+      std::fprintf(stderr,
+                   "[attn] %s dtype=%d seqs=%d groups=%d hq=%d hkv=%d d=%d items=%lld "
+                   "chunk=%d tiles=%d\n",
+                   fn, dtype, num_seqs, num_groups, h_q, h_kv, head_dim, (long long)pl.items,
+                   pl.chunk_blocks, pl.n_rt);
+    hipError_t e = attn::launch_decode_shared(dtype, p, pl.items, max_context_len,
+                                              reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, std::string(fn) + ": unexpected host exception");
   }
 }
 

@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -35,6 +36,11 @@ struct BF16 {
   __device__ static inline f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // 16x16x16: each lane holds 4 consecutive k values of one row (A) / column (B)
+  __device__ static inline f32x4 mma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack2(float x, float y) {
     f32x2 v = {x, y};
@@ -67,6 +73,10 @@ struct F16 {
   __device__ static inline f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack2(float x, float y) {
     f32x2 v = {x, y};
@@ -191,9 +201,37 @@ struct DecodeParams {
   float* lse;
   float* ws_o;    // [waves][2][group][head_dim] partial outputs
   float* ws_ml;   // [waves][2][group][2]  (max in log2 units, sum)
+  int32_t* ws_unit;  // [num_seqs][h_kv][2]: first wave of the unit, waves it spans
   int num_seqs, h_q, h_kv, group, head_dim;
   int max_blocks_per_seq;
   float scale_log2;
+  // Shared-prefix decode only (first_block == nullptr otherwise).  Sequences
+  // [group_starts[g], group_starts[g+1]) form group g; the first
+  // prefix_lens[g] tokens of each are the group's common prefix, held in the
+  // same blocks.  The prefix kernel fills seq_meta with each sequence's
+  // prefix length in blocks (first_block), its group (seq_group) and its
+  // index in the group (seq_member); the split kernel then covers only
+  // blocks at or past first_block[s].
+  const int32_t* group_starts;
+  const int32_t* prefix_lens;
+  int32_t* seq_meta;            // [3][num_seqs]
+  const int32_t* first_block;   // seq_meta
+  const int32_t* seq_group;     // seq_meta + num_seqs
+  const int32_t* seq_member;    // seq_meta + 2 num_seqs
+  float* ws_suf_o;    // [num_seqs][h_q][head_dim] suffixes finished inside one wave
+  float* ws_suf_ml;   // [num_seqs][h_q][2]
+  float* ws_pre_o;    // [prefix items][32][head_dim] one partial per item and query
+  float* ws_pre_ml;   // [prefix items][32][2]
+  int num_groups;
+  int n_rt;           // 32-query tiles per (group, KV head)
+  int n_ch;           // prefix chunks per (group, KV head, query tile)
+  int chunk_blocks;   // prefix blocks per chunk
+};
+
+// Cut of the prefix work of shared-prefix decode (host side).
+struct SharedPlan {
+  int n_rt, n_ch, chunk_blocks;
+  int64_t items;   // workgroups of the prefix kernel
 };
 
 }  // namespace attn

@@ -30,6 +30,8 @@
 // whatever a partially filled block holds past the end cannot reach the
 // output.  Nothing depends on physical block ids except addresses, so results
 // are bit-identical under any block table.
+#include <algorithm>
+
 #include "common.h"
 
 namespace attn {
@@ -37,8 +39,27 @@ namespace attn {
 constexpr int kDecBS = 16;          // tokens per KV block
 constexpr int kDecMaxWaves = 2048;  // persistent waves: 8 per CU on 256 CUs (2 per SIMD)
 
-// Blocks of a sequence (one unit per KV head).
+// Blocks of a sequence.
 __device__ inline int seq_blocks(int ctx) { return ctx > 0 ? (ctx + kDecBS - 1) / kDecBS : 0; }
+// Blocks of one (sequence, KV head) unit: the sequence's blocks from table
+// entry fb on (fb = 0, or in shared-prefix decode the blocks of the group's
+// prefix, which the prefix kernel covers).
+__device__ inline int unit_blocks(int ctx, int fb) {
+  const int nb = seq_blocks(ctx) - fb;
+  return nb > 0 ? nb : 0;
+}
+__device__ inline int first_block_of(const DecodeParams& p, int s) {
+  return p.first_block != nullptr ? p.first_block[s] : 0;
+}
+
+// Waves that take part for a list of T blocks: every wave gets at least
+// kDecMinBlocks blocks (fewer waves, fewer units cut between them), at most
+// the W launched.
+constexpr int kDecMinBlocks = 8;
+__device__ inline int used_waves(int64_t T, int W) {
+  const int64_t w = (T + kDecMinBlocks - 1) / kDecMinBlocks;
+  return w < W ? (int)w : W;
+}
 
 // Range of wave w in the flattened block list: [w T / W, (w + 1) T / W).
 __device__ inline int64_t range_start(int w, int64_t T, int W) { return (int64_t)w * T / W; }
@@ -59,7 +80,7 @@ __device__ inline int ld_meta(const int32_t* ptr, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
 }
 
-// Total blocks over all sequences and the blocks of sequences before `s`,
+// Total unit blocks over all sequences and those of sequences before `s`,
 // reduced across the 64 lanes of the calling wave (the results are uniform).
 __device__ inline void seq_block_sums(const DecodeParams& p, int s, int lane, int64_t& before,
                                       int64_t& total) {
@@ -67,7 +88,7 @@ __device__ inline void seq_block_sums(const DecodeParams& p, int s, int lane, in
   total = 0;
   for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
     const int ss = s0 + lane;
-    const int nb = (ss < p.num_seqs) ? seq_blocks(p.context_lens[ss]) : 0;
+    const int nb = (ss < p.num_seqs) ? unit_blocks(p.context_lens[ss], first_block_of(p, ss)) : 0;
     int a = (ss < s) ? nb : 0, t = nb;
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) {
@@ -99,58 +120,81 @@ void paged_decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t xp16[GP * kDecBS];
   __shared__ __attribute__((aligned(16))) float xm[2 * GP];
 
-  const int w = blockIdx.x, W = gridDim.x;
+  const int w = blockIdx.x;
   const int lane = threadIdx.x;
   const int group = p.group;
   const float c = p.scale_log2;
 
-  int64_t unused_before, total_seq_blocks;
-  seq_block_sums(p, 0, lane, unused_before, total_seq_blocks);
-  const int64_t nlist = total_seq_blocks * p.h_kv;   // blocks in the list
+  // list spans of 64 sequences (one round of loads): this lane's context,
+  // first table entry, span and the inclusive prefix sum of spans
+  struct Round {
+    int ctx, fb;
+    int64_t span, incl;
+  };
+  auto load_round = [&](int s0) {
+    Round r;
+    const int ss = s0 + lane;
+    r.ctx = ss < p.num_seqs ? p.context_lens[ss] : 0;
+    r.fb = ss < p.num_seqs ? first_block_of(p, ss) : 0;
+    r.span = (int64_t)unit_blocks(r.ctx, r.fb) * p.h_kv;
+    r.incl = r.span;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int64_t t = __shfl_up(r.incl, sh);
+      if (lane >= sh) r.incl += t;
+    }
+    return r;
+  };
+  auto lane_value = [](int64_t v, int l) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)v, l));
+  };
+  // the first round serves both the list length (up to 64 sequences) and
+  // the seek below, so the wave starts after one round trip
+  const Round r0 = load_round(0);
+  int64_t nlist;   // blocks in the list
+  if (p.num_seqs <= 64) {
+    nlist = lane_value(r0.incl, 63);
+  } else {
+    int64_t unused_before, total_seq_blocks;
+    seq_block_sums(p, 0, lane, unused_before, total_seq_blocks);
+    nlist = total_seq_blocks * p.h_kv;
+  }
   if (nlist == 0) return;
+  const int W = used_waves(nlist, gridDim.x);
+  if (w >= W) return;
   const int64_t b0 = range_start(w, nlist, W), b1 = range_start(w + 1, nlist, W);
   if (b0 >= b1) return;
 
-  // position in the unit list: unit (s, kvh), its blocks and context, the
-  // list position of its first block and the block within it
+  // position in the unit list: unit (s, kvh), its blocks, context and first
+  // table entry, the list position of its first block and the block within it
   struct Cursor {
-    int s, kvh, nblk, ctx;
+    int s, kvh, nblk, ctx, fb;
     int64_t ustart;
     int lb;
   };
-  // list position b -> cursor: the sequences' list spans are prefix-summed
-  // across the wave, 64 sequences per round of loads, and the lane whose span
-  // holds b is picked by a ballot
+  // list position b -> cursor: the lane whose span holds b is picked by a
+  // ballot, 64 sequences per round (the first round is already loaded)
   auto seek = [&](int64_t b) {
     Cursor cu{};
     int64_t base = 0;
     for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-      const int ss = s0 + lane;
-      const int ctx = ss < p.num_seqs ? p.context_lens[ss] : 0;
-      const int64_t span = (int64_t)seq_blocks(ctx) * p.h_kv;
-      int64_t incl = span;
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) {
-        const int64_t t = __shfl_up(incl, sh);
-        if (lane >= sh) incl += t;
-      }
-      const int64_t lo = base + incl - span;
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(span > 0 && b >= lo && b < lo + span);
+      const Round r = s0 == 0 ? r0 : load_round(s0);
+      const int64_t lo = base + r.incl - r.span;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(r.span > 0 && b >= lo && b < lo + r.span);
       if (hit != 0) {
         const int l = (int)__builtin_ctzll(hit);
         cu.s = s0 + l;
-        cu.ctx = __builtin_amdgcn_readlane(ctx, l);
-        cu.nblk = seq_blocks(cu.ctx);
-        const int64_t pos = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(lo >> 32), l) << 32) |
-                                      (uint32_t)__builtin_amdgcn_readlane((int)lo, l));
+        cu.ctx = __builtin_amdgcn_readlane(r.ctx, l);
+        cu.fb = __builtin_amdgcn_readlane(r.fb, l);
+        cu.nblk = unit_blocks(cu.ctx, cu.fb);
+        const int64_t pos = lane_value(lo, l);
         cu.kvh = (int)((b - pos) / cu.nblk);
         cu.ustart = pos + (int64_t)cu.kvh * cu.nblk;
         cu.lb = (int)(b - cu.ustart);
         return cu;
       }
-      const int64_t tot = __shfl(incl, 63);
-      base += (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tot >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)tot));
+      base += lane_value(r.incl, 63);
     }
     return cu;   // not reached: b lies inside the list
   };
@@ -162,8 +206,10 @@ void paged_decode_split_kernel(DecodeParams p) {
     cu.kvh = 0;
     do {   // next sequence with blocks (past the end: a harmless dummy unit)
       ++cu.s;
-      cu.ctx = (cu.s < p.num_seqs) ? ld_meta(p.context_lens, cu.s) : 1;
-      cu.nblk = seq_blocks(cu.ctx);
+      const bool in = cu.s < p.num_seqs;
+      cu.ctx = in ? ld_meta(p.context_lens, cu.s) : 1;
+      cu.fb = (in && p.first_block != nullptr) ? ld_meta(p.first_block, cu.s) : 0;
+      cu.nblk = unit_blocks(cu.ctx, cu.fb);
     } while (cu.nblk == 0);
   };
 
@@ -190,7 +236,8 @@ void paged_decode_split_kernel(DecodeParams p) {
     const char* kb = kc;
     const char* vb = vc;
     if (real) {
-      const int64_t phys = ld_meta(p.block_table, (int64_t)cu.s * p.max_blocks_per_seq + cu.lb);
+      const int64_t phys =
+          ld_meta(p.block_table, (int64_t)cu.s * p.max_blocks_per_seq + cu.fb + cu.lb);
       kb += (phys * p.h_kv + cu.kvh) * blk_bytes;
       vb += (phys * p.h_kv + cu.kvh) * blk_bytes;
     }
@@ -245,7 +292,7 @@ void paged_decode_split_kernel(DecodeParams p) {
     for (int st = 0; st < KST; ++st) acc = TT::mma16(qa[st], kr[slot][st], acc);
     // lane holds token lb*16 + lane%16, heads (lane/16)*4 + r (log2 units);
     // tokens past the context are replaced by -inf (never multiplied)
-    const int tbase = cu.lb * kDecBS;
+    const int tbase = (cu.fb + cu.lb) * kDecBS;
     const bool tv = tbase + (lane & 15) < cu.ctx;
     float sc[4];
     bool grow = false;
@@ -316,6 +363,14 @@ void paged_decode_split_kernel(DecodeParams p) {
 
   // ---- finish this wave's segment [seg_start, seg_end) of a unit ----
   auto finish = [&](const Cursor& cu, int64_t seg_start, int64_t seg_end) {
+    // the wave holding a unit's first block records where its partials are:
+    // this wave and the count of waves the unit spans
+    if (seg_start == cu.ustart && lane == 0) {
+      const int wl = wave_of(cu.ustart + cu.nblk - 1, nlist, W);
+      int32_t* ui = p.ws_unit + ((int64_t)cu.s * p.h_kv + cu.kvh) * 2;
+      ui[0] = w;
+      ui[1] = wl - w + 1;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) l_part[r] = row16_sum(l_part[r]);
     if ((lane & 15) == 0 && score_lane) {
@@ -339,7 +394,18 @@ void paged_decode_split_kernel(DecodeParams p) {
       for (int g = 0; g < group; ++g) {
         const float l = xm[GP + g], mg = xm[g];
         const int head = cu.kvh * group + g;
-        if (whole) {
+        if (whole && cu.fb > 0) {
+          // the rest of this sequence's context is a shared prefix: the
+          // combine merges this with the prefix kernel's partials
+          const int64_t row = (int64_t)cu.s * p.h_q + head;
+          float* dst = p.ws_suf_o + row * D + lane * 8;
+          *(f32x4*)dst = f32x4{oa[g][0], oa[g][1], oa[g][2], oa[g][3]};
+          *(f32x4*)(dst + 4) = f32x4{oa[g][4], oa[g][5], oa[g][6], oa[g][7]};
+          if (lane == 0) {
+            p.ws_suf_ml[row * 2 + 0] = mg;
+            p.ws_suf_ml[row * 2 + 1] = l;
+          }
+        } else if (whole) {
           const float inv = 1.f / l;
           T* og = (T*)p.o + ((int64_t)cu.s * p.h_q + head) * D + lane * 8;
           u32x4 wv;
@@ -411,45 +477,110 @@ void paged_decode_split_kernel(DecodeParams p) {
 }
 
 // One workgroup of 64 threads per (query head, sequence).  Sequences with an
-// empty context get o = 0, lse = -inf; units cut by range boundaries get their
-// partials merged: (w0, slot 1) from the wave where the unit starts, then
-// (w, slot 0) for the following waves up to the one where it ends.  Lane k
-// reads the (m, l) of partial k; the weights 2^(m_k - M) are then broadcast
-// and the O rows of eight partials are loaded at once, so the whole merge
-// costs a few dependent memory round trips whatever the number of partials.
+// empty context get o = 0, lse = -inf.  The others have their partial results
+// merged, in this order:
+//   * shared-prefix decode: the prefix kernel's partials, one per chunk of the
+//     group's prefix;
+//   * the sequence's own unit (its blocks past the prefix): nothing if it has
+//     none; one partial if it was finished inside one wave (none when there is
+//     no prefix either: the split kernel then wrote the output itself);
+//     otherwise (w0, slot 1) from the wave where the unit starts, then
+//     (w, slot 0) for each following wave up to the one where it ends.  The
+//     split kernel recorded w0 and the count.
+// Every index comes from one round of loads; lane k then reads the (m, l) of
+// partial k while the O rows of the first eight partials are fetched, so a
+// merge of up to eight partials costs two dependent memory round trips.
 template <typename TT, int D>
-__global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p, int W) {
+__global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p) {
   typedef typename TT::elem T;
   constexpr int CPL = D / 64;   // output columns per lane
   const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   const int kvh = h / p.group, g = h - kvh * p.group;
   T* og = (T*)p.o + ((int64_t)s * p.h_q + h) * D;
-  const int nb = seq_blocks(p.context_lens[s]);
-  if (nb == 0) {
+  const int ctx = p.context_lens[s];
+  int fb = 0, grp = 0, mi = 0;
+  if (p.first_block != nullptr) {
+    fb = p.first_block[s];
+    grp = p.seq_group[s];
+    mi = p.seq_member[s];
+  }
+  int w0 = 0, nu = 0;
+  if (p.ws_unit != nullptr) {
+    const int2 ui = *(const int2*)(p.ws_unit + ((int64_t)s * p.h_kv + kvh) * 2);
+    w0 = ui.x;
+    nu = ui.y;
+  }
+  if (seq_blocks(ctx) == 0) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) og[lane * CPL + c] = (T)0.f;
     if (p.lse != nullptr && lane == 0) p.lse[(int64_t)s * p.h_q + h] = -INFINITY;
     return;
   }
-  int64_t before, total;
-  seq_block_sums(p, s, lane, before, total);
-  const int64_t T_ = total * p.h_kv;
-  const int64_t ustart = before * p.h_kv + (int64_t)kvh * nb;
-  const int w0 = wave_of(ustart, T_, W), w1 = wave_of(ustart + nb - 1, T_, W);
-  if (w0 == w1) return;   // finished inside one wave
-  const int np = w1 - w0 + 1;
-  // waves with an empty range (more waves than blocks) hold no partial
-  auto has_part = [&](int k) {
-    return k == 0 || range_start(w0 + k, T_, W) < range_start(w0 + k + 1, T_, W);
+  const int nb = unit_blocks(ctx, fb);
+  // prefix partials: item (group, kvh, query tile, chunk k), query column c
+  int n_pre = 0;
+  int64_t pre_row0 = 0;
+  if (fb > 0) {
+    const int qi = mi * p.group + g;
+    n_pre = (fb + p.chunk_blocks - 1) / p.chunk_blocks;
+    pre_row0 = ((((int64_t)grp * p.h_kv + kvh) * p.n_rt + (qi >> 5)) * p.n_ch) * 32 + (qi & 31);
+  }
+  const int n_unit = nb > 0 ? nu : 0;
+  const bool unit_whole = n_unit == 1;
+  if (n_pre == 0 && unit_whole) return;   // finished inside one wave
+  const int np = n_pre + n_unit;
+  // partial k: its O row and (m, l) pair
+  auto part = [&](int k, const float*& o, const float*& ml) {
+    int64_t row;
+    if (k < n_pre) {
+      row = pre_row0 + (int64_t)k * 32;
+      o = p.ws_pre_o;
+      ml = p.ws_pre_ml;
+    } else if (unit_whole) {
+      row = (int64_t)s * p.h_q + h;
+      o = p.ws_suf_o;
+      ml = p.ws_suf_ml;
+    } else {
+      k -= n_pre;
+      row = (k == 0 ? (int64_t)w0 * 2 + 1 : (int64_t)(w0 + k) * 2) * p.group + g;
+      o = p.ws_o;
+      ml = p.ws_ml;
+    }
+    o += row * D;
+    ml += row * 2;
   };
-  auto slot_of = [&](int k) -> int64_t {
-    return k == 0 ? ((int64_t)w0 * 2 + 1) * p.group + g : ((int64_t)(w0 + k) * 2) * p.group + g;
+  auto load_o = [&](int k, float* v) {
+    const float *po, *pml;
+    part(k, po, pml);
+    const float* src = po + lane * CPL;
+    if constexpr (CPL == 2) {
+      const float2 t = *(const float2*)src;
+      v[0] = t.x;
+      v[1] = t.y;
+    } else {
+      v[0] = src[0];
+    }
   };
-  // pass 1: per-lane online merge of (m, l) over partials lane, lane + 64, ...
-  float ml = -INFINITY, ll = 0.f;
-  for (int k = lane; k < np; k += 64) {
-    if (!has_part(k)) continue;
-    const float2 v = *(const float2*)(p.ws_ml + slot_of(k) * 2);
+  // (m, l) of partial `lane` and the O rows of partials 0..7 (clamped)
+  float mk = -INFINITY, lk = 0.f;
+  if (lane < np) {
+    const float *po, *pml;
+    part(lane, po, pml);
+    const float2 v = *(const float2*)pml;
+    mk = v.x;
+    lk = v.y;
+  }
+  float v0[8][CPL];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) load_o(j < np ? j : np - 1, v0[j]);
+  // more than 64 partials: lane folds partials lane + 64, lane + 128, ...
+  // into an online (m, l); their weights are reloaded in the sum below
+  float ml = mk == -INFINITY ? -INFINITY : mk, ll = mk == -INFINITY ? 0.f : lk;
+  for (int k = lane + 64; k < np; k += 64) {
+    const float *po, *pml;
+    part(k, po, pml);
+    const float2 v = *(const float2*)pml;
+    if (v.x == -INFINITY) continue;   // a chunk with no visible token
     const float mn = fmaxf(ml, v.x);
     ll = ll * fast_exp2(ml - mn) + v.y * fast_exp2(v.x - mn);
     ml = mn;
@@ -460,29 +591,34 @@ __global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p
   float L = ml == -INFINITY ? 0.f : ll * fast_exp2(ml - M);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) L += __shfl_xor(L, sh);
-  const float inv = 1.f / L;
-  // pass 2: O = sum_k 2^(m_k - M) O_k / L, eight partials per round trip
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  // O = sum_k 2^(m_k - M) O_k / L, eight partials per round trip
   float acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   for (int c0 = 0; c0 < np; c0 += 64) {
-    const int k = c0 + lane;
-    float wl = 0.f;   // 0 marks "no partial": such slots are skipped, not scaled
-    if (k < np && has_part(k)) wl = fast_exp2(p.ws_ml[slot_of(k) * 2] - M);
+    float mw = mk;   // m of partial c0 + lane; 0 weight marks "none"
+    if (c0 > 0) {
+      mw = -INFINITY;
+      if (c0 + lane < np) {
+        const float *po, *pml;
+        part(c0 + lane, po, pml);
+        mw = pml[0];
+      }
+    }
+    const float wl = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
     const int n = np - c0 < 64 ? np - c0 : 64;
     for (int j0 = 0; j0 < n; j0 += 8) {
       float wk[8], v[8][CPL];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int kk = j0 + j < n ? j0 + j : n - 1;   // clamped: always a valid slot
+        const int kk = j0 + j < n ? j0 + j : n - 1;   // clamped: always a valid partial
         wk[j] = j0 + j < n ? __shfl(wl, kk) : 0.f;
-        const float* src = p.ws_o + slot_of(c0 + kk) * D + lane * CPL;
-        if constexpr (CPL == 2) {
-          const float2 t = *(const float2*)src;
-          v[j][0] = t.x;
-          v[j][1] = t.y;
+        if (c0 == 0 && j0 == 0) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) v[j][c] = v0[j][c];
         } else {
-          v[j][0] = src[0];
+          load_o(c0 + kk, v[j]);
         }
       }
 #pragma unroll
@@ -493,7 +629,289 @@ __global__ __launch_bounds__(64) void paged_decode_combine_kernel(DecodeParams p
   }
 #pragma unroll
   for (int c = 0; c < CPL; ++c) og[lane * CPL + c] = (T)(acc[c] * inv);
-  if (p.lse != nullptr && lane == 0) p.lse[(int64_t)s * p.h_q + h] = (M + __log2f(L)) * kLn2;
+  if (p.lse != nullptr && lane == 0)
+    p.lse[(int64_t)s * p.h_q + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Shared-prefix decode, the prefix part: the sequences of a group read their
+// common prefix from the same blocks (tutorial "Chapter 3 Advanced
+// principles", section 3.0: shared prefixes are repeated block ids), so each
+// prefix block is read once for the whole group instead of once per
+// sequence.  One workgroup of four waves per item (group, KV head, tile of 32
+// queries, chunk of chunk_blocks prefix blocks); the queries of a tile are the
+// (member, head) pairs of the group that read this KV head, member-major.
+// Wave w takes blocks w, w + 4, ... of the chunk.  Per block of 16 tokens:
+//   * S^T = K Q^T on the matrix cores (16x16x32, two 16-query tiles): K is
+//     loaded straight into the A-operand layout, Q^T stays in registers as the
+//     B operand; each lane holds one query column and four of its tokens;
+//   * online softmax per query column with a lazily raised reference max (it
+//     moves only when a score passes it by more than TAU, in log2 units);
+//   * the probabilities, rounded to the input type, are already the B
+//     operand of O^T += V^T P^T (16x16x16); V goes through LDS to be read
+//     transposed (ds_read_b64_tr_b16), four tokens of one column per lane.
+// At the end the four waves merge their (m, l, O) in LDS in a fixed order and
+// the item writes one partial per query: unnormalised O, m and l.  Tokens at
+// or past a query's context length are masked, so a context shorter than the
+// prefix is still exact (the prefix blocks must hold real data).
+//
+// Work item (g, 0, 0, 0) of every group also records each member's prefix
+// length in blocks and its group for the split and combine kernels, which run
+// after this one.
+template <typename TT, int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void paged_decode_prefix_kernel(DecodeParams p) {
+  typedef typename TT::elem T;
+  constexpr int NW = 4;                  // waves per workgroup
+  constexpr int KST = D / 32;            // k-steps of S^T = K Q^T (16x16x32)
+  constexpr int CH = D / 8;              // 16-byte chunks per K/V row
+  constexpr int ROWS = 64 / CH;          // rows per 16-byte load instruction
+  constexpr int VST = kDecBS / ROWS;     // V load instructions per block
+  constexpr int DT = D / 16;             // 16-row tiles of O^T
+  constexpr int RING = 2;                // blocks in flight per wave
+  constexpr int OP = D + 4;              // padded row of the merge area (floats)
+  constexpr float TAU = 8.0f;
+  // LDS: per wave two V staging tiles [16][D] during the loop; afterwards the
+  // same memory holds each wave's scaled O [32][OP] for the merge
+  constexpr int VBYTES = NW * 2 * kDecBS * D * 2;
+  constexpr int OBYTES = NW * 32 * OP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[VBYTES > OBYTES ? VBYTES : OBYTES];
+  __shared__ __attribute__((aligned(16))) float mls[NW][32][2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int item = blockIdx.x;
+  const int ch = item % p.n_ch;
+  item /= p.n_ch;
+  const int rt = item % p.n_rt;
+  item /= p.n_rt;
+  const int kvh = item % p.h_kv;
+  const int grp = item / p.h_kv;
+  const int gs = p.group_starts[grp], ge = p.group_starts[grp + 1];
+  // Prefix blocks covered here: whole blocks of the prefix, within the first
+  // member's context (its table row is the one read, and every slot of those
+  // blocks holds real data) and within the chunks launched.  Whatever is not
+  // covered -- also every member past the query tiles launched -- is left to
+  // the split kernel, which reads each sequence's own blocks, so a too-small
+  // host bound costs speed, not correctness.
+  const int ctx0 = ge > gs ? p.context_lens[gs] : 0;
+  int pblocks = max(0, min(p.prefix_lens[grp], ctx0)) / kDecBS;
+  pblocks = min(pblocks, min(p.n_ch * p.chunk_blocks, p.max_blocks_per_seq));
+  if (kvh == 0 && rt == 0 && ch == 0) {
+    for (int m = gs + tid; m < ge; m += 256) {
+      const bool covered = (int64_t)(m - gs + 1) * p.group <= (int64_t)p.n_rt * 32;
+      p.seq_meta[m] = covered ? pblocks : 0;
+      p.seq_meta[p.num_seqs + m] = grp;
+      p.seq_meta[2 * p.num_seqs + m] = m - gs;
+    }
+  }
+  const int j0 = ch * p.chunk_blocks;
+  const int j1 = min(pblocks, j0 + p.chunk_blocks);
+  const int rows = (ge - gs) * p.group;
+  if (j0 >= j1 || rt * 32 >= rows) return;
+  const float c = p.scale_log2;
+
+  // ---- the query columns of this lane: c = qt * 16 + lane % 16 ----
+  u32x4 qb[2][KST];
+  int ctxq[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = rt * 32 + qt * 16 + (lane & 15);
+    const bool valid = qi < rows;
+    const int m = valid ? qi / p.group : 0;
+    const int s = gs + m;
+    const int head = kvh * p.group + (qi - m * p.group);
+    ctxq[qt] = valid ? p.context_lens[s] : 0;
+    const T* qg = (const T*)p.q + ((int64_t)s * p.h_q + head) * D + (lane >> 4) * 8;
+#pragma unroll
+    for (int st = 0; st < KST; ++st) {
+      qb[qt][st] = u32x4{0, 0, 0, 0};
+      if (valid) qb[qt][st] = *(const u32x4*)(qg + 32 * st);
+    }
+  }
+
+  // ---- loads of one prefix block: K into the A-operand layout (token
+  // lane % 16, d = 32 st + 8 (lane / 16)), V rows as they are in memory ----
+  const char* kc = (const char*)p.k_cache;
+  const char* vc = (const char*)p.v_cache;
+  const int64_t blk_bytes = (int64_t)kDecBS * D * 2;
+  const uint32_t kl = (uint32_t)((lane & 15) * D + (lane >> 4) * 8) * 2u;
+  const uint32_t vl = (uint32_t)((lane / CH) * D + (lane % CH) * 8) * 2u;
+  const int mine = (j1 - j0 - w + NW - 1) / NW;   // this wave's blocks: j0 + w + NW i
+  const int64_t trow = (int64_t)gs * p.max_blocks_per_seq;
+  u32x4 kr[RING][KST], vr[RING][VST];
+  // a refill past this wave's blocks uses an empty resource: the loads still
+  // issue, in the same order, but return zeros without touching memory
+  auto issue = [&](int i, int slot) {
+    const bool real = i < mine;
+    const char* kb = kc;
+    const char* vb = vc;
+    if (real) {
+      const int64_t phys = ld_meta(p.block_table, trow + j0 + w + NW * i);
+      kb += (phys * p.h_kv + kvh) * blk_bytes;
+      vb += (phys * p.h_kv + kvh) * blk_bytes;
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, real ? (uint32_t)blk_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, real ? (uint32_t)blk_bytes : 0u);
+#pragma unroll
+    for (int st = 0; st < KST; ++st) kr[slot][st] = buf_load16(rk, kl + st * 64);
+#pragma unroll
+    for (int st = 0; st < VST; ++st) vr[slot][st] = buf_load16(rv, vl + st * ROWS * D * 2);
+  };
+
+  // ---- LDS V staging, [token][d] with 16-byte chunk c of row r stored at
+  // c ^ vsw(r), so that the transposing reads of 16 rows hit distinct banks ----
+  uint16_t* vst = (uint16_t*)smem + w * 2 * kDecBS * D;
+  auto vsw = [](int r) { return (2 * r) & (CH - 1); };
+  const int vw_row = lane / CH, vw_chunk = lane % CH;
+  // transposing read of O^T tile dt: within each 16-lane group (g4 = lane / 16)
+  // lane i = 4 j + q points at token 4 g4 + j, columns 16 dt + 4 q .. + 3;
+  // the read leaves lane i with tokens 4 g4 .. 4 g4 + 3 of column 16 dt + i
+  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2), tr_q = lane & 3;
+  auto tr_ofs = [&](int dt) {
+    return tr_row * D + (((2 * dt + (tr_q >> 1)) ^ vsw(tr_row)) * 8) + (tr_q & 1) * 4;
+  };
+
+  float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  f32x4 oacc[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](int i, int slot) {
+    const int j = j0 + w + NW * i;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int st = 0; st < KST; ++st)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) acc[qt] = TT::mma16(kr[slot][st], qb[qt][st], acc[qt]);
+    // lane: query column qt * 16 + lane % 16, tokens tb + r
+    const int tb = j * kDecBS + 4 * (lane >> 4);
+    float sc[2][4];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[qt][r] = tb + r < ctxq[qt] ? acc[qt][r] * c : -INFINITY;
+        grow = grow || sc[qt][r] > m_ref[qt] + TAU;
+      }
+    // ---- rare: a score passed its column's reference by more than TAU ----
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float bm = fmaxf(fmaxf(sc[qt][0], sc[qt][1]), fmaxf(sc[qt][2], sc[qt][3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const bool up = bm > m_ref[qt] + TAU;
+        const float alpha = fast_exp2(up ? m_ref[qt] - bm : 0.f);
+        m_ref[qt] = up ? bm : m_ref[qt];
+        l_part[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+      }
+    }
+    // probabilities relative to the reference, rounded as they enter P V
+    u32x2 pb[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mm = m_ref[qt] == -INFINITY ? 0.f : m_ref[qt];
+      pb[qt].x = TT::pack2(fast_exp2(sc[qt][0] - mm), fast_exp2(sc[qt][1] - mm));
+      pb[qt].y = TT::pack2(fast_exp2(sc[qt][2] - mm), fast_exp2(sc[qt][3] - mm));
+      l_part[qt] = TT::sum2(pb[qt].y, TT::sum2(pb[qt].x, l_part[qt]));
+    }
+    // V to LDS, then O^T += V^T P^T
+    uint16_t* vt = vst + (i & 1) * kDecBS * D;
+    lds_order();
+#pragma unroll
+    for (int st = 0; st < VST; ++st) {
+      const int r = st * ROWS + vw_row;
+      *(u32x4*)(vt + r * D + ((vw_chunk ^ vsw(r)) * 8)) = vr[slot][st];
+    }
+    lds_order();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vt + tr_ofs(dt))));
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = TT::mma16k16(a, pb[qt], oacc[dt][qt]);
+    }
+  };
+
+  // ---- stream this wave's blocks through the ring ----
+#pragma unroll
+  for (int r = 0; r < RING; ++r) issue(r, r);
+  int i = 0;
+  for (; i + RING <= mine; i += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      process(i + r, r);
+      issue(i + r + RING, r);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r)
+    if (i + r < mine) process(i + r, r);
+
+  // ---- merge the four waves: M = max m_w, O = sum 2^(m_w - M) O_w ----
+  float l_col[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float x = l_part[qt];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    l_col[qt] = x;
+  }
+  __syncthreads();   // every wave is done with its V staging
+  if (lane < 16) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      mls[w][qt * 16 + lane][0] = m_ref[qt];
+      mls[w][qt * 16 + lane][1] = l_col[qt];
+    }
+  }
+  __syncthreads();
+  float* mo = (float*)smem;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int col = qt * 16 + (lane & 15);
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][col][0]);
+    const float f = m_ref[qt] == -INFINITY ? 0.f : fast_exp2(m_ref[qt] - M);
+    float* dst = mo + (w * 32 + col) * OP + 4 * (lane >> 4);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *(f32x4*)(dst + 16 * dt) = oacc[dt][qt] * f;
+  }
+  __syncthreads();
+  // wave w writes query columns 8 w .. 8 w + 7: 8 lanes per column, D / 8
+  // consecutive floats per lane
+  {
+    constexpr int PL = D / 8;
+    const int col = w * 8 + (lane >> 3), d0 = (lane & 7) * PL;
+    if (rt * 32 + col < rows) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) M = fmaxf(M, mls[v][col][0]);
+      float L = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float mv = mls[v][col][0];
+        L += mv == -INFINITY ? 0.f : mls[v][col][1] * fast_exp2(mv - M);
+      }
+      const int64_t row = ((((int64_t)grp * p.h_kv + kvh) * p.n_rt + rt) * p.n_ch + ch) * 32 + col;
+      float* dst = p.ws_pre_o + row * D + d0;
+#pragma unroll
+      for (int e = 0; e < PL; e += 4) {
+        f32x4 x = *(const f32x4*)(mo + col * OP + d0 + e);
+#pragma unroll
+        for (int v = 1; v < NW; ++v) x += *(const f32x4*)(mo + (v * 32 + col) * OP + d0 + e);
+        *(f32x4*)(dst + e) = x;
+      }
+      if ((lane & 7) == 0) {
+        p.ws_pre_ml[row * 2 + 0] = M;
+        p.ws_pre_ml[row * 2 + 1] = L;
+      }
+    }
+  }
 }
 
 // Persistent waves for these sizes: one per block of the largest possible
@@ -508,7 +926,8 @@ size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int
       h_q % h_kv != 0)
     return 0;
   const int64_t slots = (int64_t)decode_waves(num_seqs, h_kv, max_context_len) * 2 * (h_q / h_kv);
-  return (size_t)(slots * head_dim * 4 + slots * 2 * 4);
+  // partial O rows, their (m, l) pairs, then (first wave, wave count) per unit
+  return (size_t)(slots * head_dim * 4 + slots * 2 * 4 + (int64_t)num_seqs * h_kv * 2 * 4);
 }
 
 template <typename TT, int D, int GP>
@@ -521,7 +940,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, int W, hipStream_t stre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((paged_decode_combine_kernel<TT, D>), dim3(p.h_q, p.num_seqs), dim3(64), 0,
-                     stream, p, W);
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -543,6 +962,44 @@ hipError_t launch_decode(int dtype, const DecodeParams& p, int max_context_len,
   const int W = decode_waves(p.num_seqs, p.h_kv, max_context_len);
   if (dtype == 2) return launch_decode_d<BF16>(p, W, stream);
   return launch_decode_d<F16>(p, W, stream);
+}
+
+// Shared-prefix decode: how the prefix work is cut.  Query tiles of 32 cover
+// the largest group; chunks are sized so that the largest possible prefix
+// work gives about 512 workgroups (two per CU), with 8 to 64 blocks per
+// chunk (a multiple of the 4 waves).
+SharedPlan shared_plan(int num_groups, int max_group_size, int h_q, int h_kv,
+                       int max_prefix_len) {
+  SharedPlan pl{};
+  const int64_t rows = (int64_t)max_group_size * (h_q / h_kv);
+  pl.n_rt = (int)std::max<int64_t>(1, (rows + 31) / 32);
+  const int64_t pb = std::max(0, max_prefix_len) / kDecBS;
+  const int64_t total = (int64_t)num_groups * h_kv * pl.n_rt * pb;
+  int64_t cb = (total + 511) / 512;
+  cb = (cb + 3) / 4 * 4;
+  pl.chunk_blocks = (int)std::min<int64_t>(64, std::max<int64_t>(8, cb));
+  pl.n_ch = (int)std::max<int64_t>(1, (pb + pl.chunk_blocks - 1) / pl.chunk_blocks);
+  pl.items = (int64_t)num_groups * h_kv * pl.n_rt * pl.n_ch;
+  return pl;
+}
+
+template <typename TT>
+static hipError_t launch_prefix_d(const DecodeParams& p, int64_t items, hipStream_t stream) {
+  if (p.head_dim == 64)
+    hipLaunchKernelGGL((paged_decode_prefix_kernel<TT, 64>), dim3((unsigned)items), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_prefix_kernel<TT, 128>), dim3((unsigned)items), dim3(256), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared(int dtype, const DecodeParams& p, int64_t items,
+                                int max_context_len, hipStream_t stream) {
+  const hipError_t e = dtype == 2 ? launch_prefix_d<BF16>(p, items, stream)
+                                  : launch_prefix_d<F16>(p, items, stream);
+  if (e != hipSuccess) return e;
+  return launch_decode(dtype, p, max_context_len, stream);
 }
 
 }  // namespace attn

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* element types of q, k, v, o and the KV cache */
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -167,6 +167,72 @@ int paged_attn_decode(int dtype,
                       int max_blocks_per_seq, int max_context_len, int num_blocks,
                       float softmax_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace paged_attn_decode_shared needs for these sizes
+ * (the partials of both parts and a little per-sequence metadata).  Returns 0
+ * for invalid sizes.
+ */
+size_t paged_attn_decode_shared_workspace_size(int num_seqs, int num_groups, int max_group_size,
+                                               int h_q, int h_kv, int head_dim,
+                                               int max_context_len, int max_prefix_len);
+
+/*
+ * paged_attn_decode_shared -- paged_attn_decode for sequences that share a
+ * prefix: the parallel-sampling and beam-search case of the tutorial
+ * "Chapter 3 Advanced principles: performance model and numerical
+ * stability" (section 3.0), where several sequences hold the same leading
+ * block ids.  It computes what paged_attn_decode computes, for the same
+ * arguments, but reads each shared prefix block once per group instead of
+ * once per sequence.
+ *
+ * Arguments as for paged_attn_decode, plus:
+ *   group_starts        device [num_groups + 1] int32, non-decreasing, with
+ *                       group_starts[0] == 0 and group_starts[num_groups] ==
+ *                       num_seqs: group g is sequences group_starts[g] ..
+ *                       group_starts[g + 1] - 1 (a group may be empty; an
+ *                       unshared sequence is a group of one with prefix 0).
+ *   prefix_lens         device [num_groups] int32, tokens of the group's
+ *                       common prefix, 0 <= prefix_lens[g] <= max_prefix_len
+ *                       and <= the context length of every member.  The
+ *                       first prefix_lens[g] / block_size table entries of
+ *                       every member of group g must equal those of the
+ *                       group's first member (the same physical blocks:
+ *                       that is what "shared" means); the prefix kernel reads
+ *                       them from the first member's row.  Only the prefix's
+ *                       whole blocks are read once per group; a partial last
+ *                       block is read per sequence like the rest.
+ *   num_groups          >= 1 (when num_seqs > 0).
+ *   max_group_size      host-side upper bound of the group sizes.
+ *   max_prefix_len      host-side upper bound of prefix_lens, at most
+ *                       max_context_len.
+ *   workspace           at least paged_attn_decode_shared_workspace_size(
+ *                       num_seqs, num_groups, max_group_size, h_q, h_kv,
+ *                       head_dim, max_context_len, max_prefix_len) bytes,
+ *                       16-byte aligned; contents on entry do not matter.
+ *
+ * Three kernels are enqueued.  The prefix kernel gives each group's queries
+ * that read one KV head (members x query heads, in tiles of 32) one pass
+ * over the group's prefix blocks, in chunks, on the matrix cores, and leaves
+ * one partial result per chunk and query.  The split kernel of
+ * paged_attn_decode then runs over each sequence's remaining blocks, and the
+ * combine kernel merges all partials of a (sequence, query head) by their
+ * log-sum-exp.  The result equals paged_attn_decode's up to the order of
+ * floating-point accumulation, and does not depend on which physical blocks
+ * hold the data.  If the sharing contract is broken (different ids in a
+ * member's prefix) the member's output uses the first member's prefix
+ * blocks.  Host-side errors as for paged_attn_decode.
+ */
+int paged_attn_decode_shared(int dtype,
+                             const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* context_lens,
+                             const int32_t* group_starts, const int32_t* prefix_lens,
+                             void* o, float* lse,
+                             int num_seqs, int num_groups, int max_group_size,
+                             int h_q, int h_kv, int head_dim, int block_size,
+                             int max_blocks_per_seq, int max_context_len, int max_prefix_len,
+                             int num_blocks, float softmax_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

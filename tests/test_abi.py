@@ -24,6 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "paged_attn_decode", "paged_attn_decode_workspace_size",
+              "paged_attn_decode_shared", "paged_attn_decode_shared_workspace_size",
               "attn_last_error", "attn_abi_version"):
         assert n in names
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ea.abi_version() == 2
+    assert ea.abi_version() == 3
 
 
 def test_workspace_size():
@@ -44,9 +45,11 @@ def test_workspace_size():
     # per block of the largest possible block list
     assert ea.paged_attn_decode_workspace_size(0, 32, 8, 128, 8192) == 0
     assert ea.paged_attn_decode_workspace_size(64, 32, 0, 128, 8192) == 0
-    assert ea.paged_attn_decode_workspace_size(64, 32, 8, 128, 8192) == 2048 * 2 * 4 * 130 * 4
+    # plus (first wave, wave count) per (sequence, KV head)
+    assert ea.paged_attn_decode_workspace_size(64, 32, 8, 128, 8192) == \
+        2048 * 2 * 4 * 130 * 4 + 64 * 8 * 8
     # 2 seqs x 1 kv head x ceil(513/16) = 33 blocks -> 66 waves
-    assert ea.paged_attn_decode_workspace_size(2, 4, 1, 64, 513) == 66 * 2 * 4 * 66 * 4
+    assert ea.paged_attn_decode_workspace_size(2, 4, 1, 64, 513) == 66 * 2 * 4 * 66 * 4 + 2 * 8
 
 
 FAKE = 1 << 20          # a 16-byte aligned, never dereferenced address
@@ -127,6 +130,59 @@ def test_paged_decode_rejects(kw, code):
 
 def test_paged_decode_no_sequences_is_noop():
     assert _dec(S=0, q=None, o=None, ctx=None)[0] == 0
+
+
+def _dsh(dtype=2, q=FAKE, k=FAKE, v=FAKE, table=FAKE, ctx=FAKE, gst=FAKE, plen=FAKE, o=FAKE,
+         lse=None, S=64, G=8, mgs=8, h_q=32, h_kv=8, d=128, bs=16, mbps=512, mcl=8192, mpl=4096,
+         nb=100, scale=0.088, ws=FAKE, ws_bytes=None):
+    L = ea.lib()
+    if ws_bytes is None:
+        ws_bytes = L.paged_attn_decode_shared_workspace_size(S, G, mgs, h_q, h_kv, d, mcl, mpl)
+    code = L.paged_attn_decode_shared(dtype, q, k, v, table, ctx, gst, plen, o, lse, S, G, mgs,
+                                      h_q, h_kv, d, bs, mbps, mcl, mpl, nb, scale, ws, ws_bytes,
+                                      None)
+    return code, L.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 3),
+    (dict(h_q=64, h_kv=2), 3),
+    (dict(bs=8), 3),
+    (dict(G=0), 2),
+    (dict(mgs=0), 2),
+    (dict(G=-1), 2),
+    (dict(mpl=-16), 2),
+    (dict(mpl=8193), 2),             # prefix bound above the context bound
+    (dict(gst=None), 1),
+    (dict(plen=None), 1),
+    (dict(ctx=None), 1),
+    (dict(ws=None), 4),
+    (dict(ws_bytes=1000), 4),
+    (dict(gst=FAKE + 2), 5),
+    (dict(ws=FAKE + 4), 5),
+])
+def test_paged_decode_shared_rejects(kw, code):
+    got, msg = _dsh(**kw)
+    assert got == code, msg
+    assert msg.startswith("paged_attn_decode_shared")
+
+
+def test_paged_decode_shared_no_sequences_is_noop():
+    assert _dsh(S=0, G=0, mgs=0, q=None, o=None, ctx=None, gst=None, plen=None)[0] == 0
+
+
+def test_shared_workspace_size():
+    L = ea.lib()
+    assert L.paged_attn_decode_shared_workspace_size(0, 8, 8, 32, 8, 128, 8192, 4096) == 0
+    assert L.paged_attn_decode_shared_workspace_size(64, 0, 8, 32, 8, 128, 8192, 4096) == 0
+    # 8 groups x 8 members x 4 heads = one 32-query tile per (group, KV head);
+    # 16,384 prefix blocks in all -> 32 blocks per chunk, 8 chunks: 512 items
+    split = L.paged_attn_decode_workspace_size(64, 32, 8, 128, 4352)
+    suf = 64 * 32 * 130 * 4
+    pre = 512 * 32 * 130 * 4
+    meta = 3 * 64 * 4
+    assert L.paged_attn_decode_shared_workspace_size(64, 8, 8, 32, 8, 128, 4352, 4096) == \
+        split + suf + pre + meta
 
 
 def test_last_error_cleared_on_success():

@@ -139,6 +139,11 @@ class DecodeInputs:
     dtype: str
     k_logical: list = field(default_factory=list)  # per sequence [ctx][Hkv][d]
     v_logical: list = field(default_factory=list)
+    # shared-prefix groups (None when the inputs have no group structure):
+    # group g is sequences group_starts[g] .. group_starts[g+1]-1, whose first
+    # prefix_lens[g] tokens are the same logical data
+    group_starts: torch.Tensor = None   # [G + 1] int32
+    prefix_lens: torch.Tensor = None    # [G] int32
 
     @property
     def max_context_len(self):
@@ -243,6 +248,52 @@ def decode_config4(seed=4, nan_fill=True):
                          max_blocks_per_seq=c["ctx_hi"] // c["block_size"])
 
 
+def shared_prefix_inputs(groups, h_q, h_kv, d, block_size, dtype, seed, private=False,
+                         nan_fill=True, spare_blocks=0, shuffle=True, max_blocks_per_seq=None,
+                         scale=None):
+    """Decode inputs for groups of sequences that share a prefix.
+
+    ``groups`` is a list of ``(prefix_len, [suffix_len of each member])``.
+    Member ``i`` of group ``g`` has context ``prefix_len + suffix_len``; its
+    first ``prefix_len`` K/V rows are the group's prefix.  With
+    ``private=False`` the prefix's whole blocks are one set of physical blocks
+    repeated in every member's table row (a partial last prefix block also
+    holds the member's own suffix tokens, so it stays private); with
+    ``private=True`` every member owns copies.  Draw order: per group the
+    prefix K then V ``[prefix_len][Hkv][d]``, then per member its q
+    ``[Hq][d]``, suffix K then suffix V; then the block permutation.
+    """
+    rng = np.random.default_rng(seed)
+    qs, kl, vl = [], [], []
+    shared = {}
+    starts, plens = [0], []
+    for g, (plen, suffixes) in enumerate(groups):
+        kp = _round(rng.standard_normal((plen, h_kv, d)), dtype)
+        vp = _round(rng.standard_normal((plen, h_kv, d)), dtype)
+        for sl in suffixes:
+            s = len(qs)
+            qs.append(_round(rng.standard_normal((h_q, d)), dtype))
+            ks = _round(rng.standard_normal((sl, h_kv, d)), dtype)
+            vs = _round(rng.standard_normal((sl, h_kv, d)), dtype)
+            kl.append(torch.cat([kp, ks], 0))
+            vl.append(torch.cat([vp, vs], 0))
+            if not private:
+                for lb in range(plen // block_size):
+                    shared[(s, lb)] = ("prefix", g, lb)
+        starts.append(len(qs))
+        plens.append(plen)
+    kc, vc, table, ctx = build_paged(kl, vl, block_size, rng=rng,
+                                     shared_blocks=shared if not private else None,
+                                     max_blocks_per_seq=max_blocks_per_seq, nan_fill=nan_fill,
+                                     spare_blocks=spare_blocks, shuffle=shuffle)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q = torch.stack(qs) if qs else torch.zeros((0, h_q, d), dtype=DTYPES[dtype])
+    return DecodeInputs(q, kc, vc, table, ctx, block_size, float(scale), dtype, kl, vl,
+                        torch.tensor(starts, dtype=torch.int32),
+                        torch.tensor(plens, dtype=torch.int32))
+
+
 def decode_config5(seed=5, nan_fill=True, private=False):
     """8 groups x 8 sequences sharing a 4096-token prefix per group.
 
@@ -250,33 +301,13 @@ def decode_config5(seed=5, nan_fill=True, private=False):
     prefix blocks of a group are the same physical ids in all 8 tables (3072
     blocks in the pool).  With ``private=True`` the same logical data is laid
     out with every sequence owning copies of its prefix (17408 blocks), for
-    the shared == private check.  Draw order: per group the prefix K then V,
-    then per sequence its q, suffix K then suffix V, then the permutation.
+    the shared == private check.  Draw order as in
+    :func:`shared_prefix_inputs`.
     """
     c = DECODE_CONFIGS[5]
-    rng = np.random.default_rng(seed)
-    G, P = c["groups"], c["per_group"]
-    h_q, h_kv, d, bs, dt = c["h_q"], c["h_kv"], c["d"], c["block_size"], c["dtype"]
-    qs, kl, vl = [], [], []
-    shared = {}
-    for g in range(G):
-        kp = _round(rng.standard_normal((c["prefix"], h_kv, d)), dt)
-        vp = _round(rng.standard_normal((c["prefix"], h_kv, d)), dt)
-        for i in range(P):
-            s = g * P + i
-            qs.append(_round(rng.standard_normal((h_q, d)), dt))
-            ks = _round(rng.standard_normal((c["suffix"], h_kv, d)), dt)
-            vs = _round(rng.standard_normal((c["suffix"], h_kv, d)), dt)
-            kl.append(torch.cat([kp, ks], 0))
-            vl.append(torch.cat([vp, vs], 0))
-            if not private:
-                for lb in range(c["prefix"] // bs):
-                    shared[(s, lb)] = ("prefix", g, lb)
-    kc, vc, table, ctx = build_paged(kl, vl, bs, rng=rng,
-                                     shared_blocks=shared if not private else None,
-                                     nan_fill=nan_fill)
-    return DecodeInputs(torch.stack(qs), kc, vc, table, ctx, bs, 1.0 / math.sqrt(d), dt,
-                        kl, vl)
+    groups = [(c["prefix"], [c["suffix"]] * c["per_group"])] * c["groups"]
+    return shared_prefix_inputs(groups, c["h_q"], c["h_kv"], c["d"], c["block_size"],
+                                c["dtype"], seed, private=private, nan_fill=nan_fill)
 
 
 def decode_bytes(context_lens, h_kv, d, elem_bytes=2):
