@@ -11,14 +11,18 @@ Prints one JSON line:
   roofline       prefill kernel against the dense bf16 matrix-core peak
   decode         decode GB/s (algorithmic K/V bytes / mean decode time, split +
                  combine kernels) and its roofline against HBM bandwidth
+  shared_decode  outside the step: the shared-prefix decode workload (8 groups
+                 x 8 sequences, 4096-token common prefix, 256-token private
+                 suffixes), per-sequence decode against sharing-aware decode
   cpu_baseline   the fp64 CPU oracle timed on the host on a bounded sample
 Kernel times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB copies, for counters
-    python bench.py --write-traffic FETCH WRITE COPY_FETCH COPY_WRITE
-        # profiles/traffic.json from four rocprofv3 --pmc output directories:
-        # FETCH_SIZE and WRITE_SIZE of a bench run, then of --copy-calibration
+    python bench.py --write-traffic FETCH WRITE COPY_FETCH COPY_WRITE [SFETCH SWRITE]
+        # profiles/traffic.json from rocprofv3 --pmc output directories:
+        # FETCH_SIZE and WRITE_SIZE of a --no-shared run, then of
+        # --copy-calibration, then (optional) of an --only shared run
 """
 
 import argparse
@@ -70,18 +74,22 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the shared-prefix decode measurement (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "shared"], default=None,
                     help="run one kernel family only (for profiling)")
-    ap.add_argument("--write-traffic", nargs=4, default=None,
-                    metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--write-traffic", nargs="+", default=None, metavar="DIR")
     return ap.parse_args()
 
 
-TRAFFIC_KERNELS = {   # entry name -> kernel name prefix in rocprofv3 output
-    "attn_fwd_mfma_kernel": "void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true>",
-    "paged_decode_split_kernel": "void attn::paged_decode_split_kernel<attn::BF16, 128, 4,",
-    "paged_decode_combine_kernel": "void attn::paged_decode_combine_kernel<attn::BF16",
+TRAFFIC_KERNELS = {   # entry name -> (kernel name prefix in rocprofv3 output, run)
+    "attn_fwd_mfma_kernel": ("void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true>", "main"),
+    "paged_decode_split_kernel": ("void attn::paged_decode_split_kernel<attn::BF16, 128, 4,",
+                                  "main"),
+    "paged_decode_combine_kernel": ("void attn::paged_decode_combine_kernel<attn::BF16", "main"),
+    "paged_decode_prefix_kernel": ("void attn::paged_decode_prefix_kernel<attn::BF16, 128>",
+                                   "shared"),
 }
 
 
@@ -101,9 +109,12 @@ def _counter_kib(directory, counter, prefix):
     return float(np.mean(vals)), len(vals)
 
 
-def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, sfetch_dir=None,
+                  swrite_dir=None):
     """HBM bytes per launch: counter KiB scaled by what the same counter reads
-    for plain device copies of known size (bench.py --copy-calibration)."""
+    for plain device copies of known size (bench.py --copy-calibration).
+    Kernels of the shared-prefix decode come from the optional second pair
+    of runs (bench.py --only shared)."""
     copy_bytes = 1 << 30
     cf, _ = _counter_kib(copy_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
     cw, _ = _counter_kib(copy_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
@@ -116,9 +127,12 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
                   "source_hash." % (ff, wf),
         "fetch_factor": ff, "write_factor": wf,
     }
-    for name, prefix in TRAFFIC_KERNELS.items():
-        fk, n1 = _counter_kib(fetch_dir, "FETCH_SIZE", prefix)
-        wk, n2 = _counter_kib(write_dir, "WRITE_SIZE", prefix)
+    for name, (prefix, run) in TRAFFIC_KERNELS.items():
+        fd, wd = (fetch_dir, write_dir) if run == "main" else (sfetch_dir, swrite_dir)
+        if fd is None:
+            continue
+        fk, n1 = _counter_kib(fd, "FETCH_SIZE", prefix)
+        wk, n2 = _counter_kib(wd, "WRITE_SIZE", prefix)
         fb, wb = int(round(fk * 1024 * ff)), int(round(wk * 1024 * wf))
         out[name] = {"kernel_prefix": prefix, "source_hash": source_hash(),
                      "fetch_kib_raw": fk, "write_kib_raw": wk, "dispatches": [n1, n2],
@@ -171,6 +185,68 @@ def cpu_baseline(pre, dec, dec_bytes, pre_flops):
     }
 
 
+def shared_decode(ea, workloads, dev, reps):
+    """Per-sequence decode against sharing-aware decode on the shared-prefix
+    workload, each timed over `reps` back-to-back calls with HIP events on
+    the current stream.  GB/s are reported on the logical bytes (what a
+    per-sequence kernel reads) and on the unique bytes (each shared block
+    once)."""
+    inp = workloads.decode_config5(nan_fill=True)
+    q, kc, vc = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev)
+    tab, ctx = inp.block_table.to(dev), inp.context_lens.to(dev)
+    gs, pl = inp.group_starts.to(dev), inp.prefix_lens.to(dev)
+    S, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    G = pl.shape[0]
+    mcl = inp.max_context_len
+    mgs = int(np.diff(inp.group_starts.numpy()).max())
+    mpl = int(inp.prefix_lens.max())
+    out = torch.empty_like(q)
+    ws_plain = torch.empty(ea.paged_attn_decode_workspace_size(S, Hq, Hkv, d, mcl),
+                           dtype=torch.uint8, device=dev)
+    ws_shared = torch.empty(ea.paged_attn_decode_shared_workspace_size(S, G, mgs, Hq, Hkv, d,
+                                                                       mcl, mpl),
+                            dtype=torch.uint8, device=dev)
+
+    def plain():
+        ea.paged_attn_decode(q, kc, vc, tab, ctx, max_context_len=mcl, scale=inp.scale,
+                             out=out, workspace=ws_plain)
+
+    def shared():
+        ea.paged_attn_decode_shared(q, kc, vc, tab, ctx, gs, pl, max_context_len=mcl,
+                                    max_group_size=mgs, max_prefix_len=mpl, scale=inp.scale,
+                                    out=out, workspace=ws_shared)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_plain, t_shared = timed(plain), timed(shared)
+    logical = workloads.decode_bytes(inp.context_lens.numpy(), Hkv, d)
+    unique = workloads.decode_unique_bytes(inp.block_table.numpy(), inp.context_lens.numpy(),
+                                           inp.block_size, Hkv, d)
+    return {
+        "workload": "8 groups x 8 seqs, 4096-token shared prefix + 256-token private suffix, "
+                    "Hq=32 Hkv=8 d=128 bf16 block 16 shuffled table",
+        "per_sequence_ms": t_plain, "shared_ms": t_shared, "speedup": t_plain / t_shared,
+        "logical_bytes": logical, "unique_bytes": unique,
+        "shared_logical_GBps": logical / (t_shared * 1e-3) / 1e9,
+        "shared_unique_GBps": unique / (t_shared * 1e-3) / 1e9,
+        "shared_unique_frac_of_hbm": unique / (t_shared * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "note": "back-to-back calls: the 201 MB of unique K/V largely stays in the 256 MB "
+                "last-level cache between calls",
+        "prefix_kernel_traffic": load_traffic("paged_decode_prefix_kernel"),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,6 +257,8 @@ def main():
         copy_calibration()
         return
     if args.write_traffic:
+        if len(args.write_traffic) not in (4, 6):
+            raise SystemExit("--write-traffic takes 4 or 6 directories")
         write_traffic(*args.write_traffic)
         return
     import exact_attention_34_amd as ea
@@ -207,6 +285,10 @@ def main():
 
     run_pre = args.only in (None, "prefill")
     run_dec = args.only in (None, "decode")
+    if args.only == "shared":
+        print(json.dumps({"shared_decode": shared_decode(ea, workloads, dev, args.steps)}),
+              flush=True)
+        return
 
     def step(ev=None):
         if run_pre:
@@ -271,6 +353,8 @@ def main():
                          "kernel": "paged_decode_split_kernel + paged_decode_combine_kernel",
                          "bytes_per_launch": dec_bytes},
         }
+    if args.only is None and not args.no_shared:
+        res["shared_decode"] = shared_decode(ea, workloads, dev, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre, dec, dec_bytes, pre_flops)
     print(json.dumps(res), flush=True)
