@@ -14,8 +14,10 @@ pages are cited by title and section:
   (aiknowledge.cn tutorial), section 3.0 -- PagedAttention block tables and
   prefix sharing, fp32 accumulation, block size 16.
 * "Other people's interview notes" (zzsy.me), question "explain
-  FlashAttention", part 1 (the definition Softmax(QK^T/sqrt(d_k))V) and part 2
-  (tiling and the online-softmax update of m_i, l_i and O_i).
+  FlashAttention", part 1 (the definition Softmax(QK^T/sqrt(d_k))V), part 2
+  (tiling and the online-softmax update of m_i, l_i and O_i) and part 3
+  (recomputation in the backward pass; the gradients themselves are the
+  chain rule applied to the part-1 definition).
 * "How does FlashAttention-2 differ technically from standard attention"
   (codelogiq.de FAQ) -- standard attention materialises S = QK^T; FA-2 uses
   online softmax and never stores the N x N matrix.
@@ -25,6 +27,7 @@ from .attention import (  # noqa: F401
     sdpa,
     sdpa_rows,
     sdpa_online,
+    sdpa_bwd,
     gather_paged_kv,
     paged_decode,
     allowed_keys,

@@ -190,6 +190,78 @@ def sdpa_online(q, k, v, block, scale=None, causal=False):
     return o, lse
 
 
+def _bwd_rows(q_rows, k_h, v_h, do_rows, scale, allow):
+    """Gradients contributed by a set of query rows of one head.
+
+    The pages say only that the backward pass recomputes the attention
+    probabilities from the Q, K, V blocks and the softmax statistics instead
+    of storing the N x N matrix ("Other people's interview notes", question
+    "explain FlashAttention", part 3; the codelogiq.de FAQ table, row on
+    intermediate storage).  They give no formulas, so this is the derivative
+    of the part-1 definition by the chain rule, for an upstream gradient dO of
+    the output:
+
+        S  = scale * Q K^T (invisible keys excluded)
+        P  = softmax of each row of S
+        dV = P^T dO                          (O = P V)
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))       (Jacobian of the row softmax)
+        dQ = scale * dS K,    dK = scale * dS^T Q
+
+    Returns ``(dq_rows, dk, dv)``: the rows' dQ, and their contributions to
+    the head's dK and dV.
+    """
+    s = (q_rows @ k_h.T) * scale
+    s = np.where(allow, s, -np.inf)
+    m = s.max(axis=1, initial=-np.inf)
+    has = np.isfinite(m)
+    m_safe = np.where(has, m, 0.0)
+    e = np.where(allow, np.exp(s - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    p = e / np.where(has, l, 1.0)[:, None]              # rows with no key: all 0
+    dv = p.T @ do_rows
+    dp = do_rows @ v_h.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq_rows = scale * (ds @ k_h)
+    dk = scale * (ds.T @ q_rows)
+    return dq_rows, dk, dv
+
+
+def sdpa_bwd(q, k, v, do, scale=None, causal=False):
+    """Gradients of :func:`sdpa`'s output with respect to q, k and v.
+
+    ``do`` is the upstream gradient of the output, ``[B][Nq][Hq][d]``.  Rows
+    are taken in chunks of 2048 (:func:`_bwd_rows`); a KV head's dK and dV sum
+    the contributions of every query head that reads it (grouped-query
+    attention, same head mapping as :func:`sdpa`).  Returns
+    ``(dq [B][Nq][Hq][d], dk [B][Nk][Hkv][d], dv [B][Nk][Hkv][d])``, float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    assert do.shape == q.shape and v.shape == k.shape and Hq % Hkv == 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    group = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if Nq == 0 or Nk == 0:
+        return dq, dk, dv
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // group
+            for r0 in range(0, Nq, _ROW_CHUNK):
+                r1 = min(Nq, r0 + _ROW_CHUNK)
+                allow = allowed_keys(Nq, Nk, causal, np.arange(r0, r1))
+                dqr, dkc, dvc = _bwd_rows(q[b, r0:r1, h, :], k[b, :, kvh, :], v[b, :, kvh, :],
+                                          do[b, r0:r1, h, :], scale, allow)
+                dq[b, r0:r1, h, :] = dqr
+                dk[b, :, kvh, :] += dkc
+                dv[b, :, kvh, :] += dvc
+    return dq, dk, dv
+
+
 def gather_paged_kv(pool, table_row, context_len, block_size):
     """Logical, contiguous K (or V) of one sequence read through its block table.
 
