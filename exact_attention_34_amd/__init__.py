@@ -18,7 +18,8 @@ import torch
 from . import build as _build
 
 __all__ = [
-    "AttnError", "lib", "abi_version", "attn_fwd", "paged_attn_decode",
+    "AttnError", "lib", "abi_version", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
+    "paged_attn_decode",
     "paged_attn_decode_workspace_size", "paged_attn_decode_shared",
     "paged_attn_decode_shared_workspace_size", "LIB_PATH",
 ]
@@ -62,6 +63,13 @@ def lib():
     L.attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp,
                            i32, i32, i32, i32, i32, i32,
                            i64p, i64p, i64p, i64p, f32, i32, vp]
+    L.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    L.attn_bwd.restype = i32
+    L.attn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                           i32, i32, i32, i32, i32, i32,
+                           i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p,
+                           f32, i32, vp, ctypes.c_size_t, vp]
     L.paged_attn_decode_workspace_size.restype = ctypes.c_size_t
     L.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.paged_attn_decode.restype = i32
@@ -142,6 +150,56 @@ def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=F
     if return_lse:
         return out, lse
     return out
+
+
+def attn_bwd_workspace_size(batch, n_q, h_q):
+    """Bytes of workspace :func:`attn_bwd` needs (0 if none)."""
+    return int(lib().attn_bwd_workspace_size(batch, n_q, h_q))
+
+
+def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Gradients (dq, dk, dv) of :func:`attn_fwd` for the upstream gradient ``do``.
+
+    ``q``, ``o``, ``do``: ``[B][Nq][Hq][d]``; ``k``, ``v``: ``[B][Nk][Hkv][d]``
+    (any strides with the last axis contiguous), float16 or bfloat16; ``o`` and
+    ``lse`` (``[B][Hq][Nq]`` float32, contiguous) as returned by
+    ``attn_fwd(..., return_lse=True)`` for the same inputs.  The outputs
+    default to new contiguous tensors.  Asynchronous on the current stream.
+    """
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("attn_bwd takes float16 or bfloat16 tensors")
+    for t in (k, v, o, do):
+        if t.dtype != q.dtype:
+            raise ValueError("all tensors must share one dtype")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if o.shape != q.shape or do.shape != q.shape or v.shape != k.shape or k.shape[0] != B \
+            or k.shape[3] != d:
+        raise ValueError("q, o, do must be [B][Nq][Hq][d] and k, v [B][Nk][Hkv][d]")
+    if lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B][Hq][Nq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    for t in (q, k, v, o, do, lse, dq, dk, dv):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must be on the same GPU")
+    need = attn_bwd_workspace_size(B, Nq, Hq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = lib().attn_bwd(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Nq, Nk, Hq, Hkv, d,
+                          _strides3(q), _strides3(k), _strides3(v), _strides3(o), _strides3(do),
+                          _strides3(dq), _strides3(dk), _strides3(dv), float(scale),
+                          int(bool(causal)), _ptr(workspace), ws_bytes, _stream(q.device))
+    _check(code)
+    return dq, dk, dv
 
 
 def paged_attn_decode_workspace_size(num_seqs, h_q, h_kv, head_dim, max_context_len):

@@ -15,7 +15,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
-SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

@@ -13,6 +13,8 @@ namespace attn {
 hipError_t launch_prefill(int dtype, int head_dim, bool causal, const FwdParams& p,
                           hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeParams& p, int max_context_len, hipStream_t stream);
+hipError_t launch_backward(int dtype, int head_dim, bool causal, const BwdParams& p,
+                           hipStream_t stream);
 hipError_t launch_decode_shared(int dtype, const DecodeParams& p, int64_t items,
                                 int max_context_len, hipStream_t stream);
 size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int max_context_len);
@@ -218,6 +220,106 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_ERR_HIP, "attn_fwd: unexpected host exception");
+  }
+}
+
+size_t attn_bwd_workspace_size(int batch, int n_q, int h_q) {
+  if (batch <= 0 || n_q <= 0 || h_q <= 0) return 0;
+  return align16((size_t)batch * h_q * n_q * 4);
+}
+
+int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+             const void* d_o, const float* lse, void* dq, void* dk, void* dv, int batch, int n_q,
+             int n_k, int h_q, int h_kv, int head_dim, const int64_t* q_stride,
+             const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
+             const int64_t* do_stride, const int64_t* dq_stride, const int64_t* dk_stride,
+             const int64_t* dv_stride, float softmax_scale, int causal, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  const char* fn = "attn_bwd";
+  try {
+    g_last_error.clear();
+    const std::string f(fn);
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": dtype must be ATTN_F16 or ATTN_BF16");
+    if (batch < 0 || n_q < 0 || n_k < 0 || h_q < 0 || h_kv < 0 || head_dim < 0)
+      return fail(ATTN_ERR_SHAPE, f + ": sizes must be non-negative");
+    if (h_kv == 0 || (h_q % h_kv) != 0)
+      return fail(ATTN_ERR_SHAPE, f + ": h_q must be a positive multiple of h_kv");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, f + ": causal must be 0 or 1");
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+      return fail(ATTN_ERR_SHAPE, f + ": softmax_scale must be finite and positive");
+    if (batch == 0 || h_q == 0 || (n_q == 0 && n_k == 0)) return ATTN_OK;
+    const bool has_q = n_q > 0, has_k = n_k > 0;
+    if (has_q && (q == nullptr || o == nullptr || d_o == nullptr || lse == nullptr || dq == nullptr))
+      return fail(ATTN_ERR_NULL, f + ": q, o, d_o, lse and dq must not be NULL");
+    if (has_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+      return fail(ATTN_ERR_NULL, f + ": k, v, dk and dv must not be NULL");
+    if (q_stride == nullptr || k_stride == nullptr || v_stride == nullptr || o_stride == nullptr ||
+        do_stride == nullptr || dq_stride == nullptr || dk_stride == nullptr ||
+        dv_stride == nullptr)
+      return fail(ATTN_ERR_NULL, f + ": stride arrays must not be NULL");
+    const void* ptrs[9] = {q, k, v, o, d_o, dq, dk, dv, workspace};
+    for (const void* ptr : ptrs)
+      if (ptr != nullptr && !aligned16(ptr))
+        return fail(ATTN_ERR_ALIGN, f + ": tensors and workspace must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return fail(ATTN_ERR_ALIGN, f + ": lse must be 4-byte aligned");
+    const int64_t* strides[8] = {q_stride, k_stride, v_stride, o_stride,
+                                 do_stride, dq_stride, dk_stride, dv_stride};
+    for (const int64_t* st : strides)
+      for (int i = 0; i < 3; ++i) {
+        if (st[i] < 0) return fail(ATTN_ERR_SHAPE, f + ": strides must be non-negative");
+        if ((st[i] * 2) % 16 != 0)
+          return fail(ATTN_ERR_ALIGN, f + ": batch/sequence/head strides must be multiples of 16 bytes");
+      }
+    // Q, dO, K and V tiles are addressed with 32-bit byte offsets inside one
+    // (batch, head) slice, including up to one tile past its end
+    if (((int64_t)n_k + 128) * std::max(k_stride[1], v_stride[1]) * 2 >= ((int64_t)1 << 31) ||
+        ((int64_t)n_q + 128) * std::max(q_stride[1], do_stride[1]) * 2 >= ((int64_t)1 << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": one (batch, head) slice spans >= 2 GiB");
+    if (h_q > 65535 || batch > 65535 ||
+        (int64_t)((n_q + 127) / 128) * batch * h_q >= ((int64_t)1 << 31) ||
+        (int64_t)((n_k + 127) / 128) * batch * h_kv >= ((int64_t)1 << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": problem too large for one launch");
+    const size_t need = attn_bwd_workspace_size(batch, n_q, h_q);
+    int rc = check_workspace(fn, workspace, workspace_bytes, need);
+    if (rc != ATTN_OK) return rc;
+
+    attn::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dout = d_o; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.delta = static_cast<float*>(workspace);
+    p.qs_b = q_stride[0]; p.qs_n = q_stride[1]; p.qs_h = q_stride[2];
+    p.ks_b = k_stride[0]; p.ks_n = k_stride[1]; p.ks_h = k_stride[2];
+    p.vs_b = v_stride[0]; p.vs_n = v_stride[1]; p.vs_h = v_stride[2];
+    p.os_b = o_stride[0]; p.os_n = o_stride[1]; p.os_h = o_stride[2];
+    p.dos_b = do_stride[0]; p.dos_n = do_stride[1]; p.dos_h = do_stride[2];
+    p.dqs_b = dq_stride[0]; p.dqs_n = dq_stride[1]; p.dqs_h = dq_stride[2];
+    p.dks_b = dk_stride[0]; p.dks_n = dk_stride[1]; p.dks_h = dk_stride[2];
+    p.dvs_b = dv_stride[0]; p.dvs_n = dv_stride[1]; p.dvs_h = dv_stride[2];
+    p.batch = batch; p.n_q = n_q; p.n_k = n_k; p.h_q = h_q; p.h_kv = h_kv;
+    p.group = h_q / h_kv;
+    auto extent = [&](int n, int64_t pitch) -> uint32_t {
+      return n > 0 ? (uint32_t)(((int64_t)(n - 1) * pitch + head_dim) * 2) : 0u;
+    };
+    p.q_bytes = extent(n_q, q_stride[1]);
+    p.do_bytes = extent(n_q, do_stride[1]);
+    p.k_bytes = extent(n_k, k_stride[1]);
+    p.v_bytes = extent(n_k, v_stride[1]);
+    p.scale = softmax_scale;
+    p.scale_log2 = softmax_scale * attn::kLog2e;
+    if (debug_enabled())
+      std::fprintf(stderr, "[attn] %s dtype=%d b=%d nq=%d nk=%d hq=%d hkv=%d d=%d causal=%d\n", fn,
+                   dtype, batch, n_q, n_k, h_q, h_kv, head_dim, causal);
+    hipError_t e = attn::launch_backward(dtype, head_dim, causal != 0, p,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, f + ": launch failed: " + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, std::string(fn) + ": unexpected host exception");
   }
 }
 

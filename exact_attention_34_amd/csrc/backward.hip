@@ -1,0 +1,481 @@
+// Backward pass of exact attention (bf16 / fp16, gfx950 matrix cores).
+//
+// The forward pass keeps no N x N matrix, so the backward pass recomputes
+// the probabilities tile by tile from Q, K and the forward log-sum-exp
+// ("Other people's interview notes", question "explain FlashAttention",
+// part 3: recomputation instead of storing P; the codelogiq.de FAQ table,
+// row on intermediate storage).  With S = scale Q K^T, P = softmax(S) and an
+// upstream gradient dO, the chain rule gives
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta = rowsum(dO * O),
+//     dQ = scale dS K,  dK = scale dS^T Q,
+// where rowsum(P * dP) = rowsum(dO * O) because O = P V.  P itself is
+// exp(S - lse) with the forward pass's per-row log-sum-exp: no running max is
+// needed the second time.
+//
+// Three kernels, none of them with atomics, so results are deterministic:
+//   * attn_bwd_delta_kernel: delta = rowsum(dO * O) per query row (fp32);
+//   * attn_bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, KV head)
+//     (32 per wave) and walks every query tile of every query head of the
+//     GQA group that can see them; dK and dV accumulate in registers;
+//   * attn_bwd_dq_kernel: a workgroup owns 128 query rows of one (batch,
+//     head) (32 per wave) and walks the key tiles they can see; dQ
+//     accumulates in registers.
+// Both main kernels use v_mfma_f32_32x32x16 with fp32 accumulation.  In the
+// key-owning kernel S = Q K^T leaves each lane one key column and 16 query
+// rows, so the rounded P and dS are directly the B operands of
+// dV^T = dO^T P and dK^T = Q^T dS; in the query-owning kernel S^T = K Q^T
+// leaves each lane one query column, and dS^T is the B operand of
+// dQ^T = K^T dS^T.  The transposed operands (dO^T, Q^T, K^T) are read from
+// row-major LDS tiles with ds_read_b64_tr_b16.
+#include "common.h"
+
+namespace attn {
+
+// ----------------------------------------------------------------------------
+// delta = rowsum(dO * O)
+// ----------------------------------------------------------------------------
+template <typename TT, int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
+  typedef typename TT::elem T;
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPB = 256 / CPR;   // rows per workgroup
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x * RPB + tid / CPR, c = tid % CPR;
+  const int h = blockIdx.y, b = blockIdx.z;
+  float acc = 0.f;
+  if (row < p.n_q) {
+    const u32x4 o = *(const u32x4*)((const T*)p.o + (int64_t)b * p.os_b + (int64_t)row * p.os_n +
+                                    (int64_t)h * p.os_h + c * 8);
+    const u32x4 g = *(const u32x4*)((const T*)p.dout + (int64_t)b * p.dos_b +
+                                    (int64_t)row * p.dos_n + (int64_t)h * p.dos_h + c * 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = TT::dot2(o[k], g[k], acc);
+  }
+#pragma unroll
+  for (int sh = 1; sh < CPR; sh <<= 1) acc += __shfl_xor(acc, sh);
+  if (c == 0 && row < p.n_q) p.delta[((int64_t)b * p.h_q + h) * p.n_q + row] = acc;
+}
+
+// LDS tiles of these kernels are row-major [row][d] with 16-byte chunk c of
+// row r stored at c ^ (r % 16), filled by direct buffer -> LDS loads (each
+// lane fetches the global chunk that belongs in its LDS slot).  Row reads (16
+// bytes of one row per lane, 32 rows) then hit distinct banks.
+template <int CPR>
+__device__ inline int tswz(int r) {
+  return (r & 15) & (CPR - 1);
+}
+
+// Per-lane offsets (elements) of the transposing reads of a 32-column block t
+// of such a tile: within each 16-lane group (g = lane / 16, i = lane % 16)
+// lane 4 j + q points at row 4 (g / 2) + j and columns t*32 + 16 (g % 2) + 4 q
+// .. + 3; ds_read_b64_tr_b16 then leaves lane i with rows 4 (g / 2) .. + 3 of
+// column t*32 + 16 (g % 2) + i.  The second read of a 16-row k-step is 8 rows
+// further; those rows have another swizzle, hence two offsets per block.
+// Adding 16 rows leaves the swizzle unchanged.
+template <int D>
+__device__ inline void tr_offsets(int lane, int (&ofs)[D / 32][2]) {
+  constexpr int CPR = D / 8;
+  const int vi = lane & 15, vg = lane >> 4;
+  const int r0 = (vg >> 1) * 4 + (vi >> 2);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r = r0 + 8 * half;
+      const int el = t * 32 + (vg & 1) * 16 + (vi & 3) * 4;
+      ofs[t][half] = r * D + (((el >> 3) ^ tswz<CPR>(r)) * 8) + (el & 7);
+    }
+}
+
+// A operand of a 32x32x16 product whose k index runs over 16 rows of a tile
+// (rows 4 (lane / 32) + 0..3 and 8 + 4 (lane / 32) + 0..3) and whose m index is
+// the 32 columns of block t.
+__device__ inline u32x4 tr_operand(const uint16_t* base, int ofs0, int ofs1) {
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + ofs0)));
+  const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + ofs1)));
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Stage a wave's 32 x D output block (lane = output row `col`, accumulator
+// rows = columns t*32 + 8 j + 4 hi + i) through LDS and store it as whole
+// rows: out row `row0 + r` at `dst + (row0 + r) * stride`, rows >= n skipped.
+template <typename TT, int D>
+__device__ inline void store_rows(const f32x16 (&acc)[D / 32], float mul, uint16_t* stage,
+                                  int lane, typename TT::elem* dst, int64_t stride, int row0,
+                                  int n) {
+  typedef typename TT::elem T;
+  constexpr int CPR = D / 8;
+  constexpr int OP = D + 8;   // padded row, elements
+  const int col = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w.x = TT::pack2(acc[t][4 * g + 0] * mul, acc[t][4 * g + 1] * mul);
+      w.y = TT::pack2(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
+      *(u32x2*)(stage + col * OP + t * 32 + g * 8 + hi * 4) = w;
+    }
+  lds_order();
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    const u32x4 v = *(const u32x4*)(stage + r * OP + (lane % CPR) * 8);
+    if (row0 + r < n) *(u32x4*)(dst + (int64_t)(row0 + r) * stride + (lane % CPR) * 8) = v;
+  }
+  lds_order();
+}
+
+// ----------------------------------------------------------------------------
+// dK, dV: a workgroup per (128 keys, batch, KV head)
+// ----------------------------------------------------------------------------
+template <typename TT, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
+  typedef typename TT::elem T;
+  constexpr int BK = 128, BQ = 64;        // keys per workgroup, queries per tile
+  constexpr int CPR = D / 8;
+  constexpr int NS = D / 16;              // k-steps over d
+  constexpr int TILE = BQ * D;            // elements of a Q or dO tile
+  constexpr int LOADS = BQ * CPR / 256;   // direct loads per thread per tile
+  static_assert(LOADS * 256 == BQ * CPR, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds[2 * TILE];   // dO tiles
+  __shared__ __attribute__((aligned(16))) float lse_lds[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hi = lane >> 5;
+  // items: key tile (the first tiles see the most queries when causal), batch, KV head
+  const int bh = p.batch * p.h_kv;
+  const int kt = blockIdx.x / bh, rem = blockIdx.x - kt * bh;
+  const int b = rem / p.h_kv, kvh = rem - b * p.h_kv;
+  const int k0 = kt * BK;
+  const int kcol = k0 + wave * 32 + col;   // this lane's key
+  const int off = p.n_k - p.n_q;
+  const float c = p.scale_log2;
+
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (column =
+  // key, k = d chunk 2 s + hi)
+  const T* Kg = (const T*)p.k + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
+  const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
+  u32x4 kf[NS], vf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = vf[s] = u32x4{0, 0, 0, 0};
+    if (kcol < p.n_k) {
+      kf[s] = *(const u32x4*)(Kg + (int64_t)kcol * p.ks_n + (2 * s + hi) * 8);
+      vf[s] = *(const u32x4*)(Vg + (int64_t)kcol * p.vs_n + (2 * s + hi) * 8);
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
+
+  // query tiles that see a key of this tile: q >= k0 - off when causal
+  const int qt0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
+  const int nqt = (p.n_q + BQ - 1) / BQ;
+  const int per_head = nqt > qt0 ? nqt - qt0 : 0;
+  const int ntiles = per_head * p.group;
+
+  // direct loads of the Q and dO tiles and of the tile's lse and delta rows
+  const uint32_t qrowb = (uint32_t)p.qs_n * 2u, orowb = (uint32_t)p.dos_n * 2u;
+  uint32_t qgo[LOADS], ogo[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    qgo[i] = (uint32_t)row * qrowb + (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
+    ogo[i] = (uint32_t)row * orowb + (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
+  }
+  auto load_tile = [&](int idx, int stage) {
+    const int h = kvh * p.group + idx / per_head;
+    const int q0 = (qt0 + idx % per_head) * BQ;
+    const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
+    const T* Og = (const T*)p.dout + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h;
+    const uint32_t oq = (uint32_t)q0 * qrowb, oo = (uint32_t)q0 * orowb;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(
+        (const char*)Qg + oq, __builtin_amdgcn_readfirstlane(p.q_bytes > oq ? p.q_bytes - oq : 0u));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+        (const char*)Og + oo, __builtin_amdgcn_readfirstlane(p.do_bytes > oo ? p.do_bytes - oo : 0u));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      buf_load16_lds(rq, q_lds + stage * TILE + (i * 4 + wave) * 512, qgo[i]);
+      buf_load16_lds(ro, o_lds + stage * TILE + (i * 4 + wave) * 512, ogo[i]);
+    }
+    // rows past n_q read as zero: their Q and dO rows are zero too, so they
+    // contribute nothing whatever their probabilities
+    if (wave == 0) {
+      const int64_t row = ((int64_t)b * p.h_q + h) * p.n_q + q0;
+      const uint32_t nb = (uint32_t)(p.n_q - q0) * 4u;
+      buf_load4_lds(make_rsrc(p.lse + row, nb), &lse_lds[stage][0], (uint32_t)lane * 4u);
+      buf_load4_lds(make_rsrc(p.delta + row, nb), &dl_lds[stage][0], (uint32_t)lane * 4u);
+    }
+  };
+
+  int kofs[NS];   // row reads: row col of the 32-row block, chunk 2 s + hi
+#pragma unroll
+  for (int s = 0; s < NS; ++s) kofs[s] = col * D + (((2 * s + hi) ^ tswz<CPR>(col)) * 8);
+  int tofs[D / 32][2];
+  tr_offsets<D>(lane, tofs);
+
+  if (ntiles > 0) load_tile(0, 0);
+  for (int idx = 0; idx < ntiles; ++idx) {
+    const int S = idx & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // tile idx landed; every wave is done with stage S ^ 1
+    if (idx + 1 < ntiles) load_tile(idx + 1, S ^ 1);
+    const int q0 = (qt0 + idx % per_head) * BQ;
+    const uint16_t* qb = q_lds + S * TILE;
+    const uint16_t* ob = o_lds + S * TILE;
+    // rows whose visible keys do not cover this wave's keys need the mask
+    const bool need_mask = CAUSAL && (q0 + off < k0 + wave * 32 + 31);
+#pragma unroll
+    for (int rb = 0; rb < BQ / 32; ++rb) {
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc = TT::mma32(*(const u32x4*)(qb + rb * 32 * D + kofs[s]), kf[s], sacc);
+        dpacc = TT::mma32(*(const u32x4*)(ob + rb * 32 * D + kofs[s]), vf[s], dpacc);
+      }
+      // lane: key kcol, query rows rb*32 + 8 j + 4 hi + i (register 4 j + i)
+      u32x4 pp[2], ps[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 lv = *(const f32x4*)(&lse_lds[S][rb * 32 + 8 * j + 4 * hi]);
+        const f32x4 dl = *(const f32x4*)(&dl_lds[S][rb * 32 + 8 * j + 4 * hi]);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          const int q = q0 + rb * 32 + 8 * j + 4 * hi + i;
+          const bool vis = !need_mask || kcol <= q + off;
+          pv[i] = vis ? fast_exp2(fmaf(sacc[r], c, -lv[i] * kLog2e)) : 0.f;
+          dsv[i] = pv[i] * (dpacc[r] - dl[i]);
+        }
+        // k-step j / 2 of the 32 query rows, values 4 (j % 2) .. + 3
+        pp[j >> 1][(j & 1) * 2 + 0] = TT::pack2(pv[0], pv[1]);
+        pp[j >> 1][(j & 1) * 2 + 1] = TT::pack2(pv[2], pv[3]);
+        ps[j >> 1][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
+        ps[j >> 1][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int rows = (rb * 2 + ks) * 16 * D;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          dv[t] = TT::mma32(tr_operand(ob + rows, tofs[t][0], tofs[t][1]), pp[ks], dv[t]);
+          dk[t] = TT::mma32(tr_operand(qb + rows, tofs[t][0], tofs[t][1]), ps[ks], dk[t]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dK = scale dK^T^T, dV = dV^T^T, whole rows through LDS ----
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();   // every wave is done with the tiles
+  uint16_t* stage = (wave < 2 ? q_lds : o_lds) + (wave & 1) * 32 * (D + 8);
+  static_assert(2 * 32 * (D + 8) <= 2 * TILE, "output staging fits");
+  T* dKg = (T*)p.dk + (int64_t)b * p.dks_b + (int64_t)kvh * p.dks_h;
+  T* dVg = (T*)p.dv + (int64_t)b * p.dvs_b + (int64_t)kvh * p.dvs_h;
+  store_rows<TT, D>(dk, p.scale, stage, lane, dKg, p.dks_n, k0 + wave * 32, p.n_k);
+  store_rows<TT, D>(dv, 1.f, stage, lane, dVg, p.dvs_n, k0 + wave * 32, p.n_k);
+}
+
+// ----------------------------------------------------------------------------
+// dQ: a workgroup per (128 query rows, batch, head)
+// ----------------------------------------------------------------------------
+template <typename TT, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 2)))
+void attn_bwd_dq_kernel(BwdParams p) {
+  typedef typename TT::elem T;
+  constexpr int BM = 128, BN = 64;
+  constexpr int CPR = D / 8;
+  constexpr int NS = D / 16;
+  constexpr int TILE = BN * D;
+  constexpr int LOADS = BN * CPR / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hi = lane >> 5;
+  // items: query tile (longest first when causal), batch, head
+  const int bh = p.batch * p.h_q;
+  const int rank = blockIdx.x / bh, rem = blockIdx.x - rank * bh;
+  const int b = rem / p.h_q, h = rem - b * p.h_q;
+  const int qt = CAUSAL ? (p.n_qt - 1 - rank) : rank;
+  const int q0 = qt * BM;
+  const int kvh = h / p.group;
+  const int off = p.n_k - p.n_q;
+  int kend = p.n_k;
+  if (CAUSAL) {
+    const int qlast = min(q0 + BM, p.n_q) - 1;
+    kend = min(p.n_k, max(0, qlast + off + 1));
+  }
+  const int ntiles = (kend + BN - 1) / BN;
+  const int qrow = q0 + wave * 32 + col;   // this lane's query
+  const bool qvalid = qrow < p.n_q;
+  const float c = p.scale_log2;
+
+  // Q^T and dO^T fragments: B operands of S^T = K Q^T and dP^T = V dO^T
+  const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
+  const T* Og = (const T*)p.dout + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h;
+  u32x4 qf[NS], of[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = of[s] = u32x4{0, 0, 0, 0};
+    if (qvalid) {
+      qf[s] = *(const u32x4*)(Qg + (int64_t)qrow * p.qs_n + (2 * s + hi) * 8);
+      of[s] = *(const u32x4*)(Og + (int64_t)qrow * p.dos_n + (2 * s + hi) * 8);
+    }
+  }
+  // a row past n_q has zero Q and dO: a zero lse and delta keep its (unused)
+  // column finite
+  float lse2 = 0.f, dl = 0.f;
+  if (qvalid) {
+    const int64_t row = ((int64_t)b * p.h_q + h) * p.n_q + qrow;
+    lse2 = p.lse[row] * kLog2e;
+    dl = p.delta[row];
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[t][r] = 0.f;
+
+  const T* Kg = (const T*)p.k + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
+  const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
+  const uint32_t krow = (uint32_t)p.ks_n * 2u, vrow = (uint32_t)p.vs_n * 2u;
+  uint32_t kgo[LOADS], vgo[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    kgo[i] = (uint32_t)row * krow + (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
+    vgo[i] = (uint32_t)row * vrow + (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
+  }
+  auto load_kv = [&](int kt, int stage) {
+    const uint32_t ok = (uint32_t)(kt * BN) * krow, ov = (uint32_t)(kt * BN) * vrow;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(
+        (const char*)Kg + ok, __builtin_amdgcn_readfirstlane(p.k_bytes > ok ? p.k_bytes - ok : 0u));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+        (const char*)Vg + ov, __builtin_amdgcn_readfirstlane(p.v_bytes > ov ? p.v_bytes - ov : 0u));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      buf_load16_lds(rk, ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
+      buf_load16_lds(rv, vs_lds + stage * TILE + (i * 4 + wave) * 512, vgo[i]);
+    }
+  };
+
+  int kofs[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) kofs[s] = col * D + (((2 * s + hi) ^ tswz<CPR>(col)) * 8);
+  int tofs[D / 32][2];
+  tr_offsets<D>(lane, tofs);
+
+  if (ntiles > 0) load_kv(0, 0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int S = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < ntiles) load_kv(kt + 1, S ^ 1);
+    const uint16_t* kb = ks_lds + S * TILE;
+    const uint16_t* vb = vs_lds + S * TILE;
+    const int k0 = kt * BN;
+    const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
+    u32x4 dsb[4];   // dS^T: B operand of dQ^T += K^T dS^T, one per 16-key k-step
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc = TT::mma32(*(const u32x4*)(kb + sub * 32 * D + kofs[s]), qf[s], sacc);
+        dpacc = TT::mma32(*(const u32x4*)(vb + sub * 32 * D + kofs[s]), of[s], dpacc);
+      }
+      // lane: query qrow, keys k0 + sub*32 + 8 j + 4 hi + i (register 4 j + i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float dsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          const int key = k0 + sub * 32 + 8 * j + 4 * hi + i;
+          const bool vis = !need_mask || (key < p.n_k && (!CAUSAL || key <= qrow + off));
+          const float pv = vis ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
+          dsv[i] = pv * (dpacc[r] - dl);
+        }
+        dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
+        dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+        dq[t] = TT::mma32(tr_operand(kb + ks * 16 * D, tofs[t][0], tofs[t][1]), dsb[ks], dq[t]);
+  }
+
+  // ---- epilogue: dQ = scale dQ^T^T, whole rows through LDS ----
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint16_t* stage = (wave < 2 ? ks_lds : vs_lds) + (wave & 1) * 32 * (D + 8);
+  static_assert(2 * 32 * (D + 8) <= 2 * TILE, "output staging fits");
+  T* dQg = (T*)p.dq + (int64_t)b * p.dqs_b + (int64_t)h * p.dqs_h;
+  store_rows<TT, D>(dq, p.scale, stage, lane, dQg, p.dqs_n, q0 + wave * 32, p.n_q);
+}
+
+// ----------------------------------------------------------------------------
+// host-side launch
+// ----------------------------------------------------------------------------
+template <typename TT, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  p.n_qt = (p.n_q + 127) / 128;
+  p.n_kt = (p.n_k + 127) / 128;
+  // with no query rows dK = dV = 0; with no keys dQ = 0 (the kernels write
+  // the zeros); empty grids are not launched
+  hipError_t e = hipSuccess;
+  if (p.n_q > 0) {
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<TT, D>),
+                       dim3((p.n_q + RPB - 1) / RPB, p.h_q, p.batch), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.n_k > 0) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TT, D, CAUSAL>), dim3(p.n_kt * p.batch * p.h_kv),
+                       dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.n_q > 0) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<TT, D, CAUSAL>), dim3(p.n_qt * p.batch * p.h_q),
+                       dim3(256), 0, stream, p);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// dtype: 1 f16, 2 bf16.
+hipError_t launch_backward(int dtype, int head_dim, bool causal, const BwdParams& p,
+                           hipStream_t stream) {
+#define ATTN_BWD_D(TT)                                                        \
+  (head_dim == 64 ? (causal ? launch_bwd_t<TT, 64, true>(p, stream)           \
+                            : launch_bwd_t<TT, 64, false>(p, stream))         \
+                  : (causal ? launch_bwd_t<TT, 128, true>(p, stream)          \
+                            : launch_bwd_t<TT, 128, false>(p, stream)))
+  if (dtype == 2) return ATTN_BWD_D(BF16);
+  return ATTN_BWD_D(F16);
+#undef ATTN_BWD_D
+}
+
+}  // namespace attn

@@ -168,6 +168,11 @@ __device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            off, 0, 0, 0);
 }
+// 4 bytes per lane straight into LDS: the wave fills 256 consecutive bytes.
+__device__ inline void buf_load4_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           off, 0, 0, 0);
+}
 __device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
@@ -189,6 +194,34 @@ struct FwdParams {
   int num_items;    // n_qtiles * batch * h_q
   int xcd_chunk;    // work items kept together on one XCD (0 = no remap)
   float scale_log2;  // softmax_scale * log2(e)
+};
+
+// Backward pass (bf16 / fp16).  Element strides of (batch, sequence, head);
+// the head_dim axis is contiguous.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // [B][Hq][Nq] natural-log log-sum-exp of the forward pass
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;       // [B][Hq][Nq] workspace: rowsum(dO * O)
+  int64_t qs_b, qs_n, qs_h;
+  int64_t ks_b, ks_n, ks_h;
+  int64_t vs_b, vs_n, vs_h;
+  int64_t os_b, os_n, os_h;
+  int64_t dos_b, dos_n, dos_h;
+  int64_t dqs_b, dqs_n, dqs_h;
+  int64_t dks_b, dks_n, dks_h;
+  int64_t dvs_b, dvs_n, dvs_h;
+  int batch, n_q, n_k, h_q, h_kv, group;
+  uint32_t q_bytes, k_bytes, v_bytes, do_bytes;  // byte extents of one (batch, head) slice
+  int n_qt, n_kt;     // query / key tiles
+  float scale;        // softmax scale
+  float scale_log2;   // softmax scale * log2(e)
 };
 
 struct DecodeParams {

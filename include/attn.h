@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* element types of q, k, v, o and the KV cache */
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -110,6 +110,57 @@ int attn_fwd(int dtype,
              const int64_t* q_stride, const int64_t* k_stride,
              const int64_t* v_stride, const int64_t* o_stride,
              float softmax_scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs (one fp32 per query row and head).
+ * Returns 0 for empty or invalid sizes.
+ */
+size_t attn_bwd_workspace_size(int batch, int n_q, int h_q);
+
+/*
+ * attn_bwd -- gradients of attn_fwd's output with respect to q, k and v, for
+ * an upstream gradient d_o of the output: the backward pass with
+ * recomputation of "Other people's interview notes", question "explain
+ * FlashAttention", part 3 (no N x N matrix is stored by the forward pass or
+ * written by this one; the probabilities are recomputed tile by tile from q,
+ * k and the forward log-sum-exp).  The gradients are those of the definition
+ * O = softmax(Q K^T * softmax_scale [+ causal mask]) V:
+ *     dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),
+ *     dQ = softmax_scale dS K,  dK = softmax_scale dS^T Q,
+ * with a KV head's dK and dV summed over the query heads that read it.
+ *
+ *   dtype          ATTN_F16 or ATTN_BF16 (every tensor argument shares it).
+ *   q, o, d_o      [batch][n_q][h_q][head_dim]: the forward inputs, the
+ *                  forward output O (as attn_fwd returned it) and dO.
+ *   k, v           [batch][n_k][h_kv][head_dim].
+ *   lse            [batch][h_q][n_q] fp32, contiguous: the log-sum-exp attn_fwd
+ *                  returned for these inputs (natural log; -inf for rows with
+ *                  no visible key).
+ *   dq             like q; dk, dv like k (written; every element, zeros where
+ *                  there is nothing to sum).
+ *   x_stride[3]    element strides of (batch, sequence, head) of each tensor,
+ *                  host arrays, head_dim stride 1 (same rules as attn_fwd).
+ *   head_dim, h_q, h_kv, softmax_scale, causal, stream: as attn_fwd.
+ *   workspace      device memory of at least attn_bwd_workspace_size(batch,
+ *                  n_q, h_q) bytes, 16-byte aligned; contents on entry do not
+ *                  matter.
+ *
+ * Three kernels are enqueued: rowsum(dO * O) per query row, dK and dV (a
+ * workgroup per 128 keys walks the query tiles of every head of the GQA
+ * group), and dQ (a workgroup per 128 query rows walks the key tiles).  None
+ * uses atomics, so the results are deterministic.  batch, h_q or both n_q
+ * and n_k equal to 0 is a no-op.  Host-side errors only: ATTN_ERR_NULL,
+ * _SHAPE, _UNSUPPORTED, _ALIGN, _WORKSPACE; ATTN_ERR_HIP if a launch fails.
+ */
+int attn_bwd(int dtype,
+             const void* q, const void* k, const void* v, const void* o, const void* d_o,
+             const float* lse, void* dq, void* dk, void* dv,
+             int batch, int n_q, int n_k, int h_q, int h_kv, int head_dim,
+             const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+             const int64_t* o_stride, const int64_t* do_stride, const int64_t* dq_stride,
+             const int64_t* dk_stride, const int64_t* dv_stride,
+             float softmax_scale, int causal,
+             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace paged_attn_decode needs for these sizes (the

@@ -25,6 +25,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "paged_attn_decode", "paged_attn_decode_workspace_size",
               "paged_attn_decode_shared", "paged_attn_decode_shared_workspace_size",
+              "attn_bwd", "attn_bwd_workspace_size",
               "attn_last_error", "attn_abi_version"):
         assert n in names
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ea.abi_version() == 3
+    assert ea.abi_version() == 4
 
 
 def test_workspace_size():
@@ -183,6 +184,53 @@ def test_shared_workspace_size():
     meta = 3 * 64 * 4
     assert L.paged_attn_decode_shared_workspace_size(64, 8, 8, 32, 8, 128, 4352, 4096) == \
         split + suf + pre + meta
+
+
+def _bwd(dtype=2, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+         batch=1, n_q=128, n_k=128, h_q=4, h_kv=2, d=128, qs=(128 * 4 * 128, 4 * 128, 128),
+         ks=(128 * 2 * 128, 2 * 128, 128), scale=0.088, causal=1, ws=FAKE, ws_bytes=None):
+    L = ea.lib()
+    if ws_bytes is None:
+        ws_bytes = L.attn_bwd_workspace_size(batch, n_q, h_q)
+    st = [I64x3(*qs), I64x3(*ks), I64x3(*ks), I64x3(*qs), I64x3(*qs), I64x3(*qs), I64x3(*ks),
+          I64x3(*ks)]
+    code = L.attn_bwd(dtype, q, k, v, o, do, lse, dq, dk, dv, batch, n_q, n_k, h_q, h_kv, d, *st,
+                      scale, causal, ws, ws_bytes, None)
+    return code, L.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 3),              # fp32 backward is not built
+    (dict(d=96), 3),
+    (dict(h_q=3), 2),
+    (dict(n_k=-1), 2),
+    (dict(causal=3), 2),
+    (dict(scale=float("inf")), 2),
+    (dict(lse=None), 1),
+    (dict(dk=None), 1),
+    (dict(do=None), 1),
+    (dict(ws=None), 4),
+    (dict(ws_bytes=16), 4),
+    (dict(dq=FAKE + 8), 5),
+    (dict(lse=FAKE + 2), 5),
+    (dict(qs=(128 * 4 * 128, 4 * 128, 4)), 5),
+])
+def test_attn_bwd_rejects(kw, code):
+    got, msg = _bwd(**kw)
+    assert got == code, msg
+    assert msg.startswith("attn_bwd")
+
+
+def test_attn_bwd_empty_is_noop():
+    assert _bwd(batch=0, q=None, k=None)[0] == 0
+    assert _bwd(n_q=0, n_k=0, q=None, k=None)[0] == 0
+
+
+def test_attn_bwd_workspace_size():
+    L = ea.lib()
+    assert L.attn_bwd_workspace_size(0, 128, 4) == 0
+    assert L.attn_bwd_workspace_size(2, 100, 3) == 2 * 100 * 3 * 4 + 0   # 2400 = 16 * 150
+    assert L.attn_bwd_workspace_size(1, 5, 1) == 32                      # 20 rounded up to 16
 
 
 def test_last_error_cleared_on_success():
