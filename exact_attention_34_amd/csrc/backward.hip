@@ -15,8 +15,9 @@
 // Three kernels, none of them with atomics, so results are deterministic:
 //   * attn_bwd_delta_kernel: delta = rowsum(dO * O) per query row (fp32);
 //   * attn_bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, KV head)
-//     (32 per wave) and walks every query tile of every query head of the
-//     GQA group that can see them; dK and dV accumulate in registers;
+//     and walks every query tile of every query head of the GQA group that
+//     can see them; dK and dV accumulate in registers (eight waves: 32 keys
+//     x half of each query tile per wave);
 //   * attn_bwd_dq_kernel: a workgroup owns 128 query rows of one (batch,
 //     head) (32 per wave) and walks the key tiles they can see; dQ
 //     accumulates in registers.
@@ -87,6 +88,25 @@ __device__ inline void tr_offsets(int lane, int (&ofs)[D / 32][2]) {
     }
 }
 
+// The same offsets from two registers: block t is block t % 2 shifted by
+// 8 chunks (64 elements) for t >= 2 (d = 128), and the second read is 8 rows
+// further with the chunk bit 3 flipped (d = 128) or unchanged (d = 64).
+template <int D>
+struct TrOfs {
+  int b0, b1;   // offsets of blocks 0 and 1, first read
+  __device__ inline int at(int t, int half) const {
+    int o = ((t & 1) ? b1 : b0) + 64 * (t >> 1) + half * 8 * D;
+    if (D == 128 && half) o += (t < 2) ? 64 : -64;
+    return o;
+  }
+};
+template <int D>
+__device__ inline TrOfs<D> tr_offsets2(int lane) {
+  int ofs[D / 32][2];
+  tr_offsets<D>(lane, ofs);
+  return TrOfs<D>{ofs[0][0], ofs[1][0]};
+}
+
 // A operand of a 32x32x16 product whose k index runs over 16 rows of a tile
 // (rows 4 (lane / 32) + 0..3 and 8 + 4 (lane / 32) + 0..3) and whose m index is
 // the 32 columns of block t.
@@ -132,44 +152,65 @@ __device__ inline void store_rows(const f32x16 (&acc)[D / 32], float mul, uint16
 // ----------------------------------------------------------------------------
 // dK, dV: a workgroup per (128 keys, batch, KV head)
 // ----------------------------------------------------------------------------
+// Eight waves, two per SIMD: wave w owns keys 32 (w % 4) .. + 31 of the tile
+// and, of every 64-row query tile, rows 32 (w / 4) .. + 31.  The two waves of
+// a key group hold partial dK and dV, summed through LDS at the end (in a
+// fixed order, so the result is deterministic).
 template <typename TT, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
   typedef typename TT::elem T;
   constexpr int BK = 128, BQ = 64;        // keys per workgroup, queries per tile
+  constexpr int NT = 512;                 // threads
   constexpr int CPR = D / 8;
   constexpr int NS = D / 16;              // k-steps over d
   constexpr int TILE = BQ * D;            // elements of a Q or dO tile
-  constexpr int LOADS = BQ * CPR / 256;   // direct loads per thread per tile
-  static_assert(LOADS * 256 == BQ * CPR, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t o_lds[2 * TILE];   // dO tiles
+  constexpr int LOADS = BQ * CPR / NT;    // direct loads per thread per tile
+  static_assert(LOADS * NT == BQ * CPR, "tile split");
+  // [Q stage 0][Q stage 1][dO stage 0][dO stage 1]; reused at the end for the
+  // partial sums (4 key groups x 32 keys x D fp32 = 64 KiB at D = 128) and
+  // the output staging
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];   // this tile's V, [key][d]
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BQ];
   __shared__ __attribute__((aligned(16))) float dl_lds[2][BQ];
+  uint16_t* q_lds = tiles;
+  uint16_t* o_lds = tiles + 2 * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3, rh = wave >> 2;   // key group, query-row half
   const int col = lane & 31, hi = lane >> 5;
   // items: key tile (the first tiles see the most queries when causal), batch, KV head
   const int bh = p.batch * p.h_kv;
   const int kt = blockIdx.x / bh, rem = blockIdx.x - kt * bh;
   const int b = rem / p.h_kv, kvh = rem - b * p.h_kv;
   const int k0 = kt * BK;
-  const int kcol = k0 + wave * 32 + col;   // this lane's key
+  const int kcol = k0 + kw * 32 + col;   // this lane's key
   const int off = p.n_k - p.n_q;
   const float c = p.scale_log2;
 
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (column =
-  // key, k = d chunk 2 s + hi)
+  // K fragment: B operand of S = Q K^T (column = key, k = d chunk 2 s + hi),
+  // held in registers; V (the B operand of dP = dO V^T) is read from LDS
   const T* Kg = (const T*)p.k + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
-  u32x4 kf[NS], vf[NS];
+  u32x4 kf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    kf[s] = vf[s] = u32x4{0, 0, 0, 0};
-    if (kcol < p.n_k) {
-      kf[s] = *(const u32x4*)(Kg + (int64_t)kcol * p.ks_n + (2 * s + hi) * 8);
-      vf[s] = *(const u32x4*)(Vg + (int64_t)kcol * p.vs_n + (2 * s + hi) * 8);
+    kf[s] = u32x4{0, 0, 0, 0};
+    if (kcol < p.n_k) kf[s] = *(const u32x4*)(Kg + (int64_t)kcol * p.ks_n + (2 * s + hi) * 8);
+  }
+  {
+    // V rows k0 .. k0 + 127 in the tile layout (rows past n_k read as zero)
+    const uint32_t vrow = (uint32_t)p.vs_n * 2u, ov = (uint32_t)k0 * vrow;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+        (const char*)Vg + ov, __builtin_amdgcn_readfirstlane(p.v_bytes > ov ? p.v_bytes - ov : 0u));
+#pragma unroll
+    for (int i = 0; i < BK * CPR / NT; ++i) {
+      const int slot = (i * 8 + wave) * 64 + lane;
+      const int row = slot / CPR, pc = slot % CPR;
+      buf_load16_lds(rv, v_lds + (i * 8 + wave) * 512,
+                     (uint32_t)row * vrow + (uint32_t)((pc ^ tswz<CPR>(row)) * 16));
     }
   }
   f32x16 dk[D / 32], dv[D / 32];
@@ -186,14 +227,6 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 
   // direct loads of the Q and dO tiles and of the tile's lse and delta rows
   const uint32_t qrowb = (uint32_t)p.qs_n * 2u, orowb = (uint32_t)p.dos_n * 2u;
-  uint32_t qgo[LOADS], ogo[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int slot = (i * 4 + wave) * 64 + lane;
-    const int row = slot / CPR, pc = slot % CPR;
-    qgo[i] = (uint32_t)row * qrowb + (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
-    ogo[i] = (uint32_t)row * orowb + (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
-  }
   auto load_tile = [&](int idx, int stage) {
     const int h = kvh * p.group + idx / per_head;
     const int q0 = (qt0 + idx % per_head) * BQ;
@@ -204,10 +237,18 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         (const char*)Qg + oq, __builtin_amdgcn_readfirstlane(p.q_bytes > oq ? p.q_bytes - oq : 0u));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(
         (const char*)Og + oo, __builtin_amdgcn_readfirstlane(p.do_bytes > oo ? p.do_bytes - oo : 0u));
+    // offsets recomputed per tile (a few instructions) instead of held in
+    // registers across the loop: the empty statement hides the lane index
+    // from loop-invariant hoisting
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      buf_load16_lds(rq, q_lds + stage * TILE + (i * 4 + wave) * 512, qgo[i]);
-      buf_load16_lds(ro, o_lds + stage * TILE + (i * 4 + wave) * 512, ogo[i]);
+      const int slot = (i * 8 + wave) * 64 + ln;
+      const int row = slot / CPR, pc = slot % CPR;
+      const uint32_t cb = (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
+      buf_load16_lds(rq, q_lds + stage * TILE + (i * 8 + wave) * 512, (uint32_t)row * qrowb + cb);
+      buf_load16_lds(ro, o_lds + stage * TILE + (i * 8 + wave) * 512, (uint32_t)row * orowb + cb);
     }
     // rows past n_q read as zero: their Q and dO rows are zero too, so they
     // contribute nothing whatever their probabilities
@@ -219,83 +260,142 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  int kofs[NS];   // row reads: row col of the 32-row block, chunk 2 s + hi
-#pragma unroll
-  for (int s = 0; s < NS; ++s) kofs[s] = col * D + (((2 * s + hi) ^ tswz<CPR>(col)) * 8);
-  int tofs[D / 32][2];
-  tr_offsets<D>(lane, tofs);
-
   if (ntiles > 0) load_tile(0, 0);
   for (int idx = 0; idx < ntiles; ++idx) {
     const int S = idx & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // tile idx landed; every wave is done with stage S ^ 1
     if (idx + 1 < ntiles) load_tile(idx + 1, S ^ 1);
-    const int q0 = (qt0 + idx % per_head) * BQ;
+    const int q0 = (qt0 + idx % per_head) * BQ + rh * 32;   // this wave's first row
     const uint16_t* qb = q_lds + S * TILE;
     const uint16_t* ob = o_lds + S * TILE;
     // rows whose visible keys do not cover this wave's keys need the mask
-    const bool need_mask = CAUSAL && (q0 + off < k0 + wave * 32 + 31);
+    const bool need_mask = CAUSAL && (q0 + off < k0 + kw * 32 + 31);
+    // LDS read offsets, computed here rather than held across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int kofs[NS];   // row reads: row col of this wave's 32 query rows, chunk 2 s + hi
 #pragma unroll
-    for (int rb = 0; rb < BQ / 32; ++rb) {
-      f32x16 sacc, dpacc;
+    for (int s = 0; s < NS; ++s)
+      kofs[s] = (rh * 32 + (ln & 31)) * D + (((2 * s + (ln >> 5)) ^ tswz<CPR>(ln & 31)) * 8);
+    const TrOfs<D> tofs = tr_offsets2<D>(ln);
+    // V rows of this wave's keys: the Q row offsets moved by (kw - rh) 32 rows
+    const uint16_t* vb = v_lds + (kw - rh) * 32 * D;
+    // One matrix product per slot, its LDS operand fetched PFD slots ahead:
+    // S = Q K^T and dP = dO V^T alternate over the k-steps (slots 0 ..
+    // NSD-1), then, once P and dS are formed, dV^T += dO^T P and
+    // dK^T += Q^T dS alternate over (k-step, column block).
+    constexpr int DT = D / 32;
+    constexpr int NSD = 2 * NS, NVK = 4 * DT, NSLOT = NSD + NVK;
+    constexpr int PFD = 3;
+    auto fetch = [&](int i) -> u32x4 {
+      if (i < NSD) return *(const u32x4*)(((i & 1) ? ob : qb) + kofs[i >> 1]);
+      const int j = i - NSD, ks = j / (2 * DT), t = (j >> 1) % DT;
+      return tr_operand(((j & 1) ? qb : ob) + (rh * 2 + ks) * 16 * D, tofs.at(t, 0), tofs.at(t, 1));
+    };
+    // the B operand of a dP slot (V rows), fetched with its A operand
+    auto fetch_v = [&](int i) -> u32x4 {
+      return (i < NSD && (i & 1)) ? *(const u32x4*)(vb + kofs[i >> 1]) : u32x4{0, 0, 0, 0};
+    };
+    u32x4 opnd[NSLOT], opv[NSLOT];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.f;
+    for (int i = 0; i < PFD; ++i) {
+      opnd[i] = fetch(i);
+      opv[i] = fetch_v(i);
+    }
+    f32x16 sacc, dpacc;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc = TT::mma32(*(const u32x4*)(qb + rb * 32 * D + kofs[s]), kf[s], sacc);
-        dpacc = TT::mma32(*(const u32x4*)(ob + rb * 32 * D + kofs[s]), vf[s], dpacc);
+    for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSD; ++i) {
+      opnd[i + PFD] = fetch(i + PFD);
+      opv[i + PFD] = fetch_v(i + PFD);
+      if (i & 1)
+        dpacc = TT::mma32(opnd[i], opv[i], dpacc);
+      else
+        sacc = TT::mma32(opnd[i], kf[i >> 1], sacc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane: key kcol, query rows q0 + 8 j + 4 hi + i (register 4 j + i)
+    u32x4 pp[2], ps[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 lv = *(const f32x4*)(&lse_lds[S][rh * 32 + 8 * j + 4 * hi]);
+      const f32x4 dl = *(const f32x4*)(&dl_lds[S][rh * 32 + 8 * j + 4 * hi]);
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;
+        const int q = q0 + 8 * j + 4 * hi + i;
+        const bool vis = !need_mask || kcol <= q + off;
+        pv[i] = vis ? fast_exp2(fmaf(sacc[r], c, -lv[i] * kLog2e)) : 0.f;
+        dsv[i] = pv[i] * (dpacc[r] - dl[i]);
       }
-      // lane: key kcol, query rows rb*32 + 8 j + 4 hi + i (register 4 j + i)
-      u32x4 pp[2], ps[2];
+      // k-step j / 2 of the 32 query rows, values 4 (j % 2) .. + 3
+      pp[j >> 1][(j & 1) * 2 + 0] = TT::pack2(pv[0], pv[1]);
+      pp[j >> 1][(j & 1) * 2 + 1] = TT::pack2(pv[2], pv[3]);
+      ps[j >> 1][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
+      ps[j >> 1][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 lv = *(const f32x4*)(&lse_lds[S][rb * 32 + 8 * j + 4 * hi]);
-        const f32x4 dl = *(const f32x4*)(&dl_lds[S][rb * 32 + 8 * j + 4 * hi]);
-        float pv[4], dsv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const int q = q0 + rb * 32 + 8 * j + 4 * hi + i;
-          const bool vis = !need_mask || kcol <= q + off;
-          pv[i] = vis ? fast_exp2(fmaf(sacc[r], c, -lv[i] * kLog2e)) : 0.f;
-          dsv[i] = pv[i] * (dpacc[r] - dl[i]);
-        }
-        // k-step j / 2 of the 32 query rows, values 4 (j % 2) .. + 3
-        pp[j >> 1][(j & 1) * 2 + 0] = TT::pack2(pv[0], pv[1]);
-        pp[j >> 1][(j & 1) * 2 + 1] = TT::pack2(pv[2], pv[3]);
-        ps[j >> 1][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
-        ps[j >> 1][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int rows = (rb * 2 + ks) * 16 * D;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          dv[t] = TT::mma32(tr_operand(ob + rows, tofs[t][0], tofs[t][1]), pp[ks], dv[t]);
-          dk[t] = TT::mma32(tr_operand(qb + rows, tofs[t][0], tofs[t][1]), ps[ks], dk[t]);
-        }
-      }
+    for (int i = NSD; i < NSLOT; ++i) {
+      if (i + PFD < NSLOT) opnd[i + PFD] = fetch(i + PFD);
+      const int j = i - NSD, ks = j / (2 * DT), t = (j >> 1) % DT;
+      if (j & 1)
+        dk[t] = TT::mma32(opnd[i], ps[ks], dk[t]);
+      else
+        dv[t] = TT::mma32(opnd[i], pp[ks], dv[t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- epilogue: dK = scale dK^T^T, dV = dV^T^T, whole rows through LDS ----
+  // ---- epilogue: sum the two row halves of each key group, then write
+  // dK = scale dK^T^T and dV = dV^T^T as whole rows through LDS ----
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();   // every wave is done with the tiles
-  uint16_t* stage = (wave < 2 ? q_lds : o_lds) + (wave & 1) * 32 * (D + 8);
-  static_assert(2 * 32 * (D + 8) <= 2 * TILE, "output staging fits");
-  T* dKg = (T*)p.dk + (int64_t)b * p.dks_b + (int64_t)kvh * p.dks_h;
-  T* dVg = (T*)p.dv + (int64_t)b * p.dvs_b + (int64_t)kvh * p.dvs_h;
-  store_rows<TT, D>(dk, p.scale, stage, lane, dKg, p.dks_n, k0 + wave * 32, p.n_k);
-  store_rows<TT, D>(dv, 1.f, stage, lane, dVg, p.dvs_n, k0 + wave * 32, p.n_k);
+  float* part = (float*)tiles;   // [key group][t][4 floats of 16][lane][4]
+  static_assert(4 * (D / 32) * 16 * 64 * 4 <= 4 * TILE * 2, "partial sums fit");
+  auto merge = [&](f32x16 (&acc)[D / 32]) {
+    if (rh == 1) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *(f32x4*)(part + (((kw * (D / 32) + t) * 4 + e) * 64 + lane) * 4) =
+              f32x4{acc[t][4 * e], acc[t][4 * e + 1], acc[t][4 * e + 2], acc[t][4 * e + 3]};
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4 x = *(const f32x4*)(part + (((kw * (D / 32) + t) * 4 + e) * 64 + lane) * 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[t][4 * e + u] += x[u];
+        }
+    }
+    __syncthreads();
+  };
+  merge(dk);
+  merge(dv);
+  if (rh == 0) {
+    uint16_t* stage = tiles + kw * 32 * (D + 8);
+    static_assert(4 * 32 * (D + 8) <= 4 * TILE, "output staging fits");
+    T* dKg = (T*)p.dk + (int64_t)b * p.dks_b + (int64_t)kvh * p.dks_h;
+    T* dVg = (T*)p.dv + (int64_t)b * p.dvs_b + (int64_t)kvh * p.dvs_h;
+    store_rows<TT, D>(dk, p.scale, stage, lane, dKg, p.dks_n, k0 + kw * 32, p.n_k);
+    store_rows<TT, D>(dv, 1.f, stage, lane, dVg, p.dvs_n, k0 + kw * 32, p.n_k);
+  }
 }
 
 // ----------------------------------------------------------------------------
 // dQ: a workgroup per (128 query rows, batch, head)
 // ----------------------------------------------------------------------------
 template <typename TT, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(BwdParams p) {
   typedef typename TT::elem T;
   constexpr int BM = 128, BN = 64;
@@ -377,12 +477,6 @@ void attn_bwd_dq_kernel(BwdParams p) {
     }
   };
 
-  int kofs[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) kofs[s] = col * D + (((2 * s + hi) ^ tswz<CPR>(col)) * 8);
-  int tofs[D / 32][2];
-  tr_offsets<D>(lane, tofs);
-
   if (ntiles > 0) load_kv(0, 0);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int S = kt & 1;
@@ -393,6 +487,32 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const uint16_t* vb = vs_lds + S * TILE;
     const int k0 = kt * BN;
     const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
+    // LDS read offsets, computed here rather than held across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int kofs[NS];   // row reads: key row (ln % 32), chunk 2 s + ln / 32
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kofs[s] = (ln & 31) * D + (((2 * s + (ln >> 5)) ^ tswz<CPR>(ln & 31)) * 8);
+    const TrOfs<D> tofs = tr_offsets2<D>(ln);
+    // One matrix product per slot, its LDS operand fetched PFD slots ahead:
+    // for each 32-key half, S^T = K Q^T and dP^T = V dO^T alternate over
+    // the k-steps (then that half's dS^T is formed); then dQ^T += K^T dS^T
+    // over (k-step, column block).
+    constexpr int DT = D / 32;
+    constexpr int NSD = 2 * NS, NQ = (BN / 16) * DT, NSLOT = 2 * NSD + NQ;
+    constexpr int PFD = 3;
+    auto fetch = [&](int i) -> u32x4 {
+      if (i < 2 * NSD) {
+        const int sub = i / NSD, j = i % NSD;
+        return *(const u32x4*)(((j & 1) ? vb : kb) + sub * 32 * D + kofs[j >> 1]);
+      }
+      const int j = i - 2 * NSD, ks = j / DT, t = j % DT;
+      return tr_operand(kb + ks * 16 * D, tofs.at(t, 0), tofs.at(t, 1));
+    };
+    u32x4 opnd[NSLOT];
+#pragma unroll
+    for (int i = 0; i < PFD; ++i) opnd[i] = fetch(i);
     u32x4 dsb[4];   // dS^T: B operand of dQ^T += K^T dS^T, one per 16-key k-step
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -400,9 +520,14 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc = TT::mma32(*(const u32x4*)(kb + sub * 32 * D + kofs[s]), qf[s], sacc);
-        dpacc = TT::mma32(*(const u32x4*)(vb + sub * 32 * D + kofs[s]), of[s], dpacc);
+      for (int j = 0; j < NSD; ++j) {
+        const int i = sub * NSD + j;
+        opnd[i + PFD] = fetch(i + PFD);
+        if (j & 1)
+          dpacc = TT::mma32(opnd[i], of[j >> 1], dpacc);
+        else
+          sacc = TT::mma32(opnd[i], qf[j >> 1], sacc);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // lane: query qrow, keys k0 + sub*32 + 8 j + 4 hi + i (register 4 j + i)
 #pragma unroll
@@ -419,12 +544,15 @@ void attn_bwd_dq_kernel(BwdParams p) {
         dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
         dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-        dq[t] = TT::mma32(tr_operand(kb + ks * 16 * D, tofs[t][0], tofs[t][1]), dsb[ks], dq[t]);
+    for (int i = 2 * NSD; i < NSLOT; ++i) {
+      if (i + PFD < NSLOT) opnd[i + PFD] = fetch(i + PFD);
+      const int j = i - 2 * NSD, ks = j / DT, t = j % DT;
+      dq[t] = TT::mma32(opnd[i], dsb[ks], dq[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- epilogue: dQ = scale dQ^T^T, whole rows through LDS ----
@@ -454,7 +582,7 @@ static hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
   }
   if (p.n_k > 0) {
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TT, D, CAUSAL>), dim3(p.n_kt * p.batch * p.h_kv),
-                       dim3(256), 0, stream, p);
+                       dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.n_q > 0) {
