@@ -14,15 +14,20 @@ Prints one JSON line:
   shared_decode  outside the step: the shared-prefix decode workload (8 groups
                  x 8 sequences, 4096-token common prefix, 256-token private
                  suffixes), per-sequence decode against sharing-aware decode
+  backward       outside the step: attn_bwd on the prefill workload (its own
+                 O and log-sum-exp, a seeded dO), TFLOP/s counted as 2.5x the
+                 forward's algorithmic FLOP, against the bf16 peak
   cpu_baseline   the fp64 CPU oracle timed on the host on a bounded sample
 Kernel times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB copies, for counters
-    python bench.py --write-traffic FETCH WRITE COPY_FETCH COPY_WRITE [SFETCH SWRITE]
+    python bench.py --write-traffic FETCH WRITE COPY_FETCH COPY_WRITE [SFETCH SWRITE
+                                    [BFETCH BWRITE]]
         # profiles/traffic.json from rocprofv3 --pmc output directories:
         # FETCH_SIZE and WRITE_SIZE of a --no-shared run, then of
-        # --copy-calibration, then (optional) of an --only shared run
+        # --copy-calibration, then (optional) of an --only shared run and of
+        # an --only backward run
 """
 
 import argparse
@@ -77,7 +82,7 @@ def parse():
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-prefix decode measurement (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "shared"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward"], default=None,
                     help="run one kernel family only (for profiling)")
     ap.add_argument("--write-traffic", nargs="+", default=None, metavar="DIR")
     return ap.parse_args()
@@ -90,6 +95,8 @@ TRAFFIC_KERNELS = {   # entry name -> (kernel name prefix in rocprofv3 output, r
     "paged_decode_combine_kernel": ("void attn::paged_decode_combine_kernel<attn::BF16", "main"),
     "paged_decode_prefix_kernel": ("void attn::paged_decode_prefix_kernel<attn::BF16, 128>",
                                    "shared"),
+    "attn_bwd_dkdv_kernel": ("void attn::attn_bwd_dkdv_kernel<attn::BF16, 128, true>", "backward"),
+    "attn_bwd_dq_kernel": ("void attn::attn_bwd_dq_kernel<attn::BF16, 128, true>", "backward"),
 }
 
 
@@ -110,7 +117,7 @@ def _counter_kib(directory, counter, prefix):
 
 
 def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, sfetch_dir=None,
-                  swrite_dir=None):
+                  swrite_dir=None, bfetch_dir=None, bwrite_dir=None):
     """HBM bytes per launch: counter KiB scaled by what the same counter reads
     for plain device copies of known size (bench.py --copy-calibration).
     Kernels of the shared-prefix decode come from the optional second pair
@@ -128,7 +135,8 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, sfetch_d
         "fetch_factor": ff, "write_factor": wf,
     }
     for name, (prefix, run) in TRAFFIC_KERNELS.items():
-        fd, wd = (fetch_dir, write_dir) if run == "main" else (sfetch_dir, swrite_dir)
+        fd, wd = {"main": (fetch_dir, write_dir), "shared": (sfetch_dir, swrite_dir),
+                  "backward": (bfetch_dir, bwrite_dir)}[run]
         if fd is None:
             continue
         fk, n1 = _counter_kib(fd, "FETCH_SIZE", prefix)
@@ -247,6 +255,50 @@ def shared_decode(ea, workloads, dev, reps):
     }
 
 
+def backward(ea, pre, q, k, v, pre_flops, reps):
+    """attn_bwd on the prefill workload, timed over `reps` back-to-back calls
+    with HIP events on the current stream.  O and the log-sum-exp come from
+    attn_fwd on the same inputs; dO is seeded N(0, 1) rounded to bf16."""
+    o, lse = ea.attn_fwd(q, k, v, causal=True, scale=pre.scale, return_lse=True)
+    g = torch.Generator().manual_seed(7)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float64).to(q.dtype).to(q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, N, Hq, _ = q.shape
+    ws = torch.empty(max(1, ea.attn_bwd_workspace_size(B, N, Hq)), dtype=torch.uint8,
+                     device=q.device)
+
+    def run():
+        ea.attn_bwd(q, k, v, o, do, lse, causal=True, scale=pre.scale, dq=dq, dk=dk, dv=dv,
+                    workspace=ws)
+
+    for _ in range(3):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 2.5 * pre_flops
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": "backward of the causal prefill B=4 Hq=Hkv=16 N=2048 d=128 bf16 "
+                    "(1% Q/K rows x20)",
+        "mean_ms": ms, "value": tf, "unit": "TFLOP/s",
+        "flop_per_call": flops,
+        "flop_convention": "2.5 x forward algorithmic FLOP (dV, dP, dQ, dK and the recomputed S); "
+                           "the kernels execute 3.5 x (dP and S are recomputed for dQ)",
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "traffic": {"dkdv": load_traffic("attn_bwd_dkdv_kernel"),
+                                 "dq": load_traffic("attn_bwd_dq_kernel")},
+                     "kernel": "attn_bwd_delta_kernel + attn_bwd_dkdv_kernel + "
+                               "attn_bwd_dq_kernel <bf16,128,causal>"},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -257,8 +309,8 @@ def main():
         copy_calibration()
         return
     if args.write_traffic:
-        if len(args.write_traffic) not in (4, 6):
-            raise SystemExit("--write-traffic takes 4 or 6 directories")
+        if len(args.write_traffic) not in (4, 6, 8):
+            raise SystemExit("--write-traffic takes 4, 6 or 8 directories")
         write_traffic(*args.write_traffic)
         return
     import exact_attention_34_amd as ea
@@ -271,6 +323,14 @@ def main():
     pre_flops = workloads.prefill_flops(B, N, N, Hq, d, True)
     q, k, v = (x.to(dev) for x in (pre.q, pre.k, pre.v))
     o = torch.empty_like(q)
+    if args.only == "shared":
+        print(json.dumps({"shared_decode": shared_decode(ea, workloads, dev, args.steps)}),
+              flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps({"backward": backward(ea, pre, q, k, v, pre_flops, args.steps)}),
+              flush=True)
+        return
 
     dec = workloads.decode_config4(nan_fill=True)
     dq = dec.q.to(dev)
@@ -285,10 +345,6 @@ def main():
 
     run_pre = args.only in (None, "prefill")
     run_dec = args.only in (None, "decode")
-    if args.only == "shared":
-        print(json.dumps({"shared_decode": shared_decode(ea, workloads, dev, args.steps)}),
-              flush=True)
-        return
 
     def step(ev=None):
         if run_pre:
@@ -355,6 +411,7 @@ def main():
         }
     if args.only is None and not args.no_shared:
         res["shared_decode"] = shared_decode(ea, workloads, dev, args.steps)
+        res["backward"] = backward(ea, pre, q, k, v, pre_flops, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre, dec, dec_bytes, pre_flops)
     print(json.dumps(res), flush=True)
