@@ -21,7 +21,8 @@ __all__ = [
     "AttnError", "lib", "abi_version", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
     "paged_attn_decode",
     "paged_attn_decode_workspace_size", "paged_attn_decode_shared",
-    "paged_attn_decode_shared_workspace_size", "LIB_PATH",
+    "paged_attn_decode_shared_workspace_size", "paged_kv_write", "paged_kv_copy_blocks",
+    "BlockManager", "LIB_PATH",
 ]
 
 LIB_PATH = _build.LIB_PATH
@@ -29,7 +30,8 @@ LIB_PATH = _build.LIB_PATH
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 ERROR_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
-               4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_HIP"}
+               4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_HIP",
+               7: "ATTN_ERR_NO_BLOCKS"}
 
 
 class AttnError(RuntimeError):
@@ -82,6 +84,31 @@ def lib():
     L.paged_attn_decode_shared.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                            i32, f32, vp, ctypes.c_size_t, vp]
+    i64, i32p, i64p_ = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    L.paged_kv_write.restype = i32
+    L.paged_kv_write.argtypes = [i32, vp, vp, i64p, i64p, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.paged_kv_copy_blocks.restype = i32
+    L.paged_kv_copy_blocks.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.attn_bm_create.restype = i32
+    L.attn_bm_create.argtypes = [i32, i32, ctypes.POINTER(vp)]
+    L.attn_bm_destroy.restype = None
+    L.attn_bm_destroy.argtypes = [vp]
+    L.attn_bm_num_free.restype = i32
+    L.attn_bm_num_free.argtypes = [vp]
+    L.attn_bm_ref_count.restype = i32
+    L.attn_bm_ref_count.argtypes = [vp, i32]
+    L.attn_bm_length.restype = i64
+    L.attn_bm_length.argtypes = [vp, i64]
+    L.attn_bm_add_sequence.restype = i32
+    L.attn_bm_add_sequence.argtypes = [vp, i64]
+    L.attn_bm_fork.restype = i32
+    L.attn_bm_fork.argtypes = [vp, i64, i64]
+    L.attn_bm_append.restype = i32
+    L.attn_bm_append.argtypes = [vp, i64, i32, i32p, i32p, i32p, ctypes.POINTER(i32)]
+    L.attn_bm_free_sequence.restype = i32
+    L.attn_bm_free_sequence.argtypes = [vp, i64]
+    L.attn_bm_block_table.restype = i32
+    L.attn_bm_block_table.argtypes = [vp, i64p_, i32, i32, i32p, i32p]
     _LIB = L
     return L
 
@@ -318,3 +345,110 @@ def paged_attn_decode_shared(q, k_cache, v_cache, block_table, context_lens, gro
     if return_lse:
         return out, lse
     return out
+
+
+def _kv_strides(t):
+    if t.dim() != 3 or t.stride(-1) != 1:
+        raise ValueError("new K/V must be [tokens][h_kv][d] views with d contiguous")
+    return (ctypes.c_int64 * 2)(t.stride(0), t.stride(1))
+
+
+def paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache):
+    """Write new tokens' K/V rows (``[T][Hkv][d]``, any token/head strides)
+    into the paged caches at ``slot_mapping`` (``[T]`` int32 on the GPU;
+    slots outside the pool are skipped).  Asynchronous."""
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks][Hkv][block_size][d]")
+    NB, Hkv, bs, d = k_cache.shape
+    if k_new.shape != v_new.shape or k_new.shape[1:] != (Hkv, d):
+        raise ValueError("k_new and v_new must be [T][Hkv][d] matching the cache")
+    for t in (k_new, v_new):
+        if t.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+            raise ValueError("new K/V and caches must share one dtype")
+    if slot_mapping.dtype != torch.int32 or slot_mapping.shape != (k_new.shape[0],) \
+            or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 [T] tensor")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    code = lib().paged_kv_write(_DTYPE_CODE[k_cache.dtype], _ptr(k_new), _ptr(v_new),
+                                _kv_strides(k_new), _kv_strides(v_new), _ptr(slot_mapping),
+                                _ptr(k_cache), _ptr(v_cache), k_new.shape[0], Hkv, d, bs, NB,
+                                _stream(k_cache.device))
+    _check(code)
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, src, dst):
+    """Copy whole blocks ``src[i] -> dst[i]`` (int32 GPU tensors) in both
+    caches.  Asynchronous."""
+    NB, Hkv, bs, d = k_cache.shape
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape \
+            or src.dim() != 1:
+        raise ValueError("src and dst must be int32 [n] tensors")
+    code = lib().paged_kv_copy_blocks(_DTYPE_CODE[k_cache.dtype], _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(src), _ptr(dst), src.shape[0], Hkv, d, bs, NB,
+                                      _stream(k_cache.device))
+    _check(code)
+
+
+class BlockManager:
+    """Host bookkeeping of a paged KV cache (the C ABI's attn_bm_* calls).
+
+    ``append`` returns the slots of the new tokens and the copy-on-write block
+    copies (a list of ``(src, dst)``) to run before writing them."""
+
+    def __init__(self, num_blocks, block_size=16):
+        h = ctypes.c_void_p()
+        _check(lib().attn_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.block_size = int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().attn_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self):
+        return lib().attn_bm_num_free(self._h)
+
+    def ref_count(self, block):
+        return lib().attn_bm_ref_count(self._h, int(block))
+
+    def length(self, seq_id):
+        return lib().attn_bm_length(self._h, int(seq_id))
+
+    def add_sequence(self, seq_id):
+        _check(lib().attn_bm_add_sequence(self._h, int(seq_id)))
+
+    def fork(self, parent, child):
+        _check(lib().attn_bm_fork(self._h, int(parent), int(child)))
+
+    def append(self, seq_id, n_tokens):
+        import numpy as np
+        slots = np.zeros(max(1, n_tokens), dtype=np.int32)
+        cs, cd = ctypes.c_int32(), ctypes.c_int32()
+        n = ctypes.c_int32()
+        p32 = ctypes.POINTER(ctypes.c_int32)
+        _check(lib().attn_bm_append(self._h, int(seq_id), int(n_tokens),
+                                    slots.ctypes.data_as(p32), ctypes.byref(cs), ctypes.byref(cd),
+                                    ctypes.byref(n)))
+        return slots[:n_tokens], ([(cs.value, cd.value)] if n.value else [])
+
+    def free_sequence(self, seq_id):
+        _check(lib().attn_bm_free_sequence(self._h, int(seq_id)))
+
+    def block_table(self, seq_ids, max_blocks):
+        import numpy as np
+        ids = np.asarray(seq_ids, dtype=np.int64)
+        table = np.zeros((len(ids), max(1, max_blocks)), dtype=np.int32)
+        ctx = np.zeros(max(1, len(ids)), dtype=np.int32)
+        _check(lib().attn_bm_block_table(
+            self._h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(ids),
+            int(max_blocks), table.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return table[:, :max_blocks] if max_blocks else table[:, :0], ctx[:len(ids)]

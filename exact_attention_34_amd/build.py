@@ -15,7 +15,8 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
-SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "backward.hip"]
+SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "backward.hip", "kv_cache.hip",
+           "block_manager.cpp"]
 ARCH = "gfx950"
 
 

@@ -20,6 +20,27 @@ hipError_t launch_decode_shared(int dtype, const DecodeParams& p, int64_t items,
 size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int max_context_len);
 int decode_waves(int num_seqs, int h_kv, int max_context_len);
 SharedPlan shared_plan(int num_groups, int max_group_size, int h_q, int h_kv, int max_prefix_len);
+struct KvWriteParams {
+  const void* k_new;
+  const void* v_new;
+  int64_t ks_t, ks_h;
+  int64_t vs_t, vs_h;
+  const int32_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int n_tokens, h_kv, head_dim, block_size;
+  int64_t num_slots;
+};
+struct KvCopyParams {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src;
+  const int32_t* dst;
+  int64_t block_elems;
+  int num_blocks;
+};
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
+hipError_t launch_kv_copy(const KvCopyParams& p, int n_pairs, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -138,6 +159,14 @@ bool debug_enabled() {
 
 }  // namespace
 
+namespace attn {
+// Status and message for the calling thread (used by block_manager.cpp too).
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+}  // namespace attn
+
 extern "C" {
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
@@ -220,6 +249,74 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_ERR_HIP, "attn_fwd: unexpected host exception");
+  }
+}
+
+int paged_kv_write(int dtype, const void* k_new, const void* v_new, const int64_t* k_stride,
+                   const int64_t* v_stride, const int32_t* slot_mapping, void* k_cache,
+                   void* v_cache, int n_tokens, int h_kv, int head_dim, int block_size,
+                   int num_blocks, void* stream) {
+  const std::string f("paged_kv_write");
+  try {
+    g_last_error.clear();
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": dtype must be ATTN_F16 or ATTN_BF16");
+    if (n_tokens < 0 || h_kv <= 0 || num_blocks < 0)
+      return fail(ATTN_ERR_SHAPE, f + ": n_tokens >= 0, h_kv > 0, num_blocks >= 0 required");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+    if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, f + ": block_size must be 16");
+    if (n_tokens == 0) return ATTN_OK;
+    if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr || k_cache == nullptr ||
+        v_cache == nullptr || k_stride == nullptr || v_stride == nullptr)
+      return fail(ATTN_ERR_NULL, f + ": pointers must not be NULL");
+    const void* ptrs[4] = {k_new, v_new, k_cache, v_cache};
+    for (const void* ptr : ptrs)
+      if (!aligned16(ptr)) return fail(ATTN_ERR_ALIGN, f + ": tensors must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(slot_mapping) & 3u)
+      return fail(ATTN_ERR_ALIGN, f + ": slot_mapping must be 4-byte aligned");
+    for (int i = 0; i < 2; ++i)
+      if (k_stride[i] < 0 || v_stride[i] < 0 || (k_stride[i] * 2) % 16 || (v_stride[i] * 2) % 16)
+        return fail(ATTN_ERR_ALIGN, f + ": token and head strides must be non-negative multiples of 16 bytes");
+    if (n_tokens > 0x7fffffff / 2) return fail(ATTN_ERR_UNSUPPORTED, f + ": too many tokens");
+    attn::KvWriteParams p{k_new, v_new, k_stride[0], k_stride[1], v_stride[0], v_stride[1],
+                          slot_mapping, k_cache, v_cache, n_tokens, h_kv, head_dim, block_size,
+                          (int64_t)num_blocks * block_size};
+    hipError_t e = attn::launch_kv_write(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, f + ": launch failed: " + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, f + ": unexpected host exception");
+  }
+}
+
+int paged_kv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t* src,
+                         const int32_t* dst, int n_pairs, int h_kv, int head_dim, int block_size,
+                         int num_blocks, void* stream) {
+  const std::string f("paged_kv_copy_blocks");
+  try {
+    g_last_error.clear();
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": dtype must be ATTN_F16 or ATTN_BF16");
+    if (n_pairs < 0 || h_kv <= 0 || num_blocks < 0)
+      return fail(ATTN_ERR_SHAPE, f + ": n_pairs >= 0, h_kv > 0, num_blocks >= 0 required");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+    if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, f + ": block_size must be 16");
+    if (n_pairs == 0) return ATTN_OK;
+    if (k_cache == nullptr || v_cache == nullptr || src == nullptr || dst == nullptr)
+      return fail(ATTN_ERR_NULL, f + ": pointers must not be NULL");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+      return fail(ATTN_ERR_ALIGN, f + ": caches must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(src) & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u))
+      return fail(ATTN_ERR_ALIGN, f + ": src and dst must be 4-byte aligned");
+    attn::KvCopyParams p{k_cache, v_cache, src, dst, (int64_t)h_kv * block_size * head_dim,
+                         num_blocks};
+    hipError_t e = attn::launch_kv_copy(p, n_pairs, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, f + ": launch failed: " + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, f + ": unexpected host exception");
   }
 }
 

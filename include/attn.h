@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* element types of q, k, v, o and the KV cache */
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -67,7 +67,8 @@ enum {
   ATTN_ERR_UNSUPPORTED = 3, /* a valid but unsupported dtype / head_dim / block size / group */
   ATTN_ERR_WORKSPACE = 4,   /* decode workspace missing or smaller than required */
   ATTN_ERR_ALIGN = 5,       /* a base pointer or row stride is not 16-byte aligned */
-  ATTN_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  ATTN_ERR_NO_BLOCKS = 7    /* the block manager has too few free blocks (nothing changed) */
 };
 
 /* ABI version of the loaded library (ATTN_ABI_VERSION). */
@@ -284,6 +285,93 @@ int paged_attn_decode_shared(int dtype,
                              int max_blocks_per_seq, int max_context_len, int max_prefix_len,
                              int num_blocks, float softmax_scale,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged KV cache maintenance.  The cache layout is paged_attn_decode's:
+ * k_cache and v_cache are [num_blocks][h_kv][block_size][head_dim] (block_size
+ * 16, head_dim 64 or 128, bf16 or fp16), and logical token t of a sequence
+ * lives at slot block_table[t / block_size] * block_size + t % block_size (the
+ * tutorial "Chapter 3 Advanced principles: performance model and numerical
+ * stability", section 3.0: fixed-size blocks, per-sequence block tables,
+ * blocks shared by forked sequences and copied before a shared block is
+ * written).
+ */
+
+/*
+ * paged_kv_write -- write the K and V rows of n_tokens new tokens into their
+ * slots: for token i, k_cache[slot / block_size][h][slot % block_size][:] =
+ * k_new[i][h][:] for every KV head h, and the same for V.
+ *
+ *   k_new, v_new    device, token i head h at x_new + i * x_stride[0] +
+ *                   h * x_stride[1] (elements; head_dim contiguous), so a
+ *                   [batch][seq][h_kv][d] prefill tensor can be passed as a
+ *                   view.  x_stride: host arrays of 2.
+ *   slot_mapping    device [n_tokens] int32; a slot outside [0, num_blocks *
+ *                   block_size) (for instance -1 for padding) is skipped.
+ *   Two tokens must not name the same slot (the order of their writes is
+ *   not defined).  Asynchronous; host-side errors as for paged_attn_decode.
+ */
+int paged_kv_write(int dtype, const void* k_new, const void* v_new,
+                   const int64_t* k_stride, const int64_t* v_stride,
+                   const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                   int n_tokens, int h_kv, int head_dim, int block_size, int num_blocks,
+                   void* stream);
+
+/*
+ * paged_kv_copy_blocks -- copy whole blocks (every KV head of K and of V):
+ * block dst[i] becomes a copy of block src[i].  src, dst: device [n_pairs]
+ * int32; pairs naming a block outside [0, num_blocks) are skipped.  The
+ * destinations must be distinct and must not be sources of other pairs (the
+ * block manager's copy-on-write copies satisfy this).  Asynchronous.
+ */
+int paged_kv_copy_blocks(int dtype, void* k_cache, void* v_cache,
+                         const int32_t* src, const int32_t* dst, int n_pairs,
+                         int h_kv, int head_dim, int block_size, int num_blocks, void* stream);
+
+/*
+ * Block manager (host only; no device memory, no GPU calls).  It does the
+ * bookkeeping of a paged KV cache of num_blocks blocks: it hands out slots
+ * for new tokens, counts references per block, and, when a sequence appends
+ * to a partially filled last block that another sequence also holds, moves
+ * the sequence to a fresh block and reports the copy (source, destination)
+ * that the caller must run (paged_kv_copy_blocks) before writing the new
+ * tokens (paged_kv_write).  Full blocks stay shared.  A forked sequence
+ * shares all of its parent's blocks.  Free blocks are reused last-freed first,
+ * so the same sequence of calls gives the same block ids.  A handle is not
+ * thread-safe: one thread at a time per handle.  Errors: ATTN_ERR_NULL,
+ * ATTN_ERR_SHAPE (bad size, unknown or duplicate sequence id),
+ * ATTN_ERR_NO_BLOCKS (not enough free blocks; the call changes nothing).
+ */
+typedef struct attn_block_manager attn_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens, all free, into *out. */
+int attn_bm_create(int num_blocks, int block_size, attn_block_manager** out);
+void attn_bm_destroy(attn_block_manager* m);
+/* Free blocks; -1 for a NULL manager. */
+int attn_bm_num_free(const attn_block_manager* m);
+/* References to block (sequences holding it); -1 if out of range. */
+int attn_bm_ref_count(const attn_block_manager* m, int block);
+/* Tokens of a sequence; -1 if unknown. */
+int64_t attn_bm_length(const attn_block_manager* m, int64_t seq_id);
+/* A new, empty sequence. */
+int attn_bm_add_sequence(attn_block_manager* m, int64_t seq_id);
+/* A new sequence child holding parent's tokens and sharing its blocks. */
+int attn_bm_fork(attn_block_manager* m, int64_t parent, int64_t child);
+/*
+ * Append n_tokens tokens to seq_id: slots[i] (host, n_tokens) receives the
+ * slot of the i-th new token; copy_src[0] / copy_dst[0] (host, room for one
+ * pair) and *n_copies (0 or 1) receive the copy-on-write copy to run first.
+ */
+int attn_bm_append(attn_block_manager* m, int64_t seq_id, int n_tokens, int32_t* slots,
+                   int32_t* copy_src, int32_t* copy_dst, int* n_copies);
+/* Release a sequence; blocks no longer held by any sequence become free. */
+int attn_bm_free_sequence(attn_block_manager* m, int64_t seq_id);
+/*
+ * Block table rows (host [n][max_blocks] int32, -1 padded) and context
+ * lengths (host [n]) of n sequences, in paged_attn_decode's format.
+ */
+int attn_bm_block_table(const attn_block_manager* m, const int64_t* seq_ids, int n,
+                        int max_blocks, int32_t* table, int32_t* context_lens);
 
 #ifdef __cplusplus
 }

@@ -30,5 +30,7 @@ from .attention import (  # noqa: F401
     sdpa_bwd,
     gather_paged_kv,
     paged_decode,
+    paged_kv_write,
+    paged_kv_copy_blocks,
     allowed_keys,
 )

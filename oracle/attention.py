@@ -302,3 +302,35 @@ def paged_decode(q, k_pool, v_pool, block_table, context_lens, block_size, scale
         o[s] = oo[0, 0]
         lse[s] = ll[0, :, 0]
     return o, lse
+
+
+def paged_kv_write(k_pool, v_pool, k_new, v_new, slots, block_size):
+    """The paged KV cache after writing new tokens (numpy copies).
+
+    PagedAttention's cache keeps token t of a sequence at slot
+    ``table[t // block_size] * block_size + t % block_size`` of a pool of
+    fixed-size blocks ("Chapter 3 Advanced principles", section 3.0).  Token
+    ``i``'s rows (``k_new[i]``, ``v_new[i]``: ``[Hkv][d]``) go to slot
+    ``slots[i]``; slots outside the pool are skipped.  The pools are
+    ``[num_blocks][Hkv][block_size][d]``.
+    """
+    k_pool, v_pool = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    n_slots = k_pool.shape[0] * block_size
+    for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
+        if 0 <= slot < n_slots:
+            k_pool[slot // block_size, :, slot % block_size, :] = k_new[i]
+            v_pool[slot // block_size, :, slot % block_size, :] = v_new[i]
+    return k_pool, v_pool
+
+
+def paged_kv_copy_blocks(k_pool, v_pool, src, dst):
+    """The pools after copying block ``src[i]`` to block ``dst[i]`` (copy-on-
+    write of a shared block before it is written, same section); pairs naming
+    a block outside the pool are skipped."""
+    k_pool, v_pool = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    nb = k_pool.shape[0]
+    for s, d in zip(np.asarray(src), np.asarray(dst)):
+        if 0 <= s < nb and 0 <= d < nb:
+            k_pool[d] = k_pool[s]
+            v_pool[d] = v_pool[s]
+    return k_pool, v_pool
