@@ -22,6 +22,7 @@ __all__ = [
     "paged_attn_decode",
     "paged_attn_decode_workspace_size", "paged_attn_decode_shared",
     "paged_attn_decode_shared_workspace_size", "paged_kv_write", "paged_kv_copy_blocks",
+    "attn_fwd_paged",
     "BlockManager", "LIB_PATH",
 ]
 
@@ -85,6 +86,9 @@ def lib():
                                            i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                            i32, f32, vp, ctypes.c_size_t, vp]
     i64, i32p, i64p_ = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    L.attn_fwd_paged.restype = i32
+    L.attn_fwd_paged.argtypes = [i32, vp, i64p, vp, vp, vp, vp, vp, i64p, vp,
+                                 i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.paged_kv_write.restype = i32
     L.paged_kv_write.argtypes = [i32, vp, vp, i64p, i64p, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.paged_kv_copy_blocks.restype = i32
@@ -452,3 +456,41 @@ class BlockManager:
             int(max_blocks), table.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
             ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return table[:, :max_blocks] if max_blocks else table[:, :0], ctx[:len(ids)]
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, context_lens, max_context_len, causal=True,
+                   scale=None, out=None, lse=None, return_lse=False):
+    """Prefill over a paged KV cache: ``q`` ``[B][Nq][Hq][d]`` are the last
+    ``Nq`` tokens of each sequence, whose K/V (``context_lens[b]`` tokens, int32
+    on the GPU) are read through ``block_table`` (``[B][max_blocks]`` int32).
+    Asynchronous on the current stream."""
+    if q.dim() != 4 or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be a float16/bfloat16 [B][Nq][Hq][d] tensor")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype \
+            or v_cache.dtype != q.dtype:
+        raise ValueError("caches must be [blocks][Hkv][bs][d] of q's dtype")
+    B, Nq, Hq, d = q.shape
+    NB, Hkv, bs, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim mismatch")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32 \
+            or block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be int32 [B][max_blocks], context_lens int32 [B]")
+    for t in (k_cache, v_cache, block_table, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("caches, block_table and context_lens must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    code = lib().attn_fwd_paged(_DTYPE_CODE[q.dtype], _ptr(q), _strides3(q), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(block_table), _ptr(context_lens), _ptr(out),
+                                _strides3(out), _ptr(lse), B, Nq, Hq, Hkv, d, bs,
+                                block_table.shape[1], int(max_context_len), NB, float(scale),
+                                int(bool(causal)), _stream(q.device))
+    _check(code)
+    if return_lse:
+        return out, lse
+    return out

@@ -12,6 +12,8 @@
 namespace attn {
 hipError_t launch_prefill(int dtype, int head_dim, bool causal, const FwdParams& p,
                           hipStream_t stream);
+hipError_t launch_prefill_paged(int dtype, int head_dim, bool causal, const FwdParams& p,
+                                hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeParams& p, int max_context_len, hipStream_t stream);
 hipError_t launch_backward(int dtype, int head_dim, bool causal, const BwdParams& p,
                            hipStream_t stream);
@@ -249,6 +251,80 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_ERR_HIP, "attn_fwd: unexpected host exception");
+  }
+}
+
+int attn_fwd_paged(int dtype, const void* q, const int64_t* q_stride, const void* k_cache,
+                   const void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                   void* o, const int64_t* o_stride, float* lse, int batch, int n_q, int h_q,
+                   int h_kv, int head_dim, int block_size, int max_blocks_per_seq,
+                   int max_context_len, int num_blocks, float softmax_scale, int causal,
+                   void* stream) {
+  const std::string f("attn_fwd_paged");
+  try {
+    g_last_error.clear();
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": dtype must be ATTN_F16 or ATTN_BF16");
+    if (batch < 0 || n_q < 0 || h_q < 0 || h_kv < 0 || head_dim < 0 || max_blocks_per_seq < 0 ||
+        max_context_len < 0 || num_blocks < 0)
+      return fail(ATTN_ERR_SHAPE, f + ": sizes must be non-negative");
+    if (h_kv == 0 || (h_q % h_kv) != 0)
+      return fail(ATTN_ERR_SHAPE, f + ": h_q must be a positive multiple of h_kv");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+    if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, f + ": block_size must be 16");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, f + ": causal must be 0 or 1");
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+      return fail(ATTN_ERR_SHAPE, f + ": softmax_scale must be finite and positive");
+    if ((int64_t)max_blocks_per_seq * block_size < (int64_t)max_context_len)
+      return fail(ATTN_ERR_SHAPE, f + ": max_blocks_per_seq * block_size < max_context_len");
+    if (max_context_len > 0 && num_blocks == 0)
+      return fail(ATTN_ERR_SHAPE, f + ": num_blocks must be positive");
+    if (batch == 0 || n_q == 0 || h_q == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr || context_lens == nullptr || q_stride == nullptr ||
+        o_stride == nullptr)
+      return fail(ATTN_ERR_NULL, f + ": q, o, context_lens and strides must not be NULL");
+    if (max_context_len > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
+      return fail(ATTN_ERR_NULL, f + ": caches and block_table must not be NULL");
+    const void* ptrs[4] = {q, o, k_cache, v_cache};
+    for (const void* ptr : ptrs)
+      if (ptr != nullptr && !aligned16(ptr))
+        return fail(ATTN_ERR_ALIGN, f + ": q, o and the caches must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+      return fail(ATTN_ERR_ALIGN, f + ": block_table, context_lens and lse must be 4-byte aligned");
+    for (const int64_t* st : {q_stride, o_stride})
+      for (int i = 0; i < 3; ++i)
+        if (st[i] < 0 || (st[i] * 2) % 16 != 0)
+          return fail(ATTN_ERR_ALIGN, f + ": strides must be non-negative multiples of 16 bytes");
+    if (((int64_t)n_q + 128) * q_stride[1] * 2 >= ((int64_t)1 << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": one (batch, head) slice of q spans >= 2 GiB");
+    if ((int64_t)((n_q + 63) / 64) * batch * h_q > (int64_t)1 << 31)
+      return fail(ATTN_ERR_UNSUPPORTED, f + ": problem too large for one launch");
+    attn::FwdParams p{};
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.o = o;
+    p.lse = lse;
+    p.qs_b = q_stride[0]; p.qs_n = q_stride[1]; p.qs_h = q_stride[2];
+    p.os_b = o_stride[0]; p.os_n = o_stride[1]; p.os_h = o_stride[2];
+    p.batch = batch;
+    p.n_q = n_q;
+    p.n_k = max_context_len;
+    p.h_q = h_q;
+    p.h_kv = h_kv;
+    p.group = h_q / h_kv;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.scale_log2 = softmax_scale * attn::kLog2e;
+    hipError_t e = attn::launch_prefill_paged(dtype, head_dim, causal != 0, p,
+                                              reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, f + ": launch failed: " + hipGetErrorString(e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_ERR_HIP, f + ": unexpected host exception");
   }
 }
 

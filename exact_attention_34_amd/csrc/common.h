@@ -190,6 +190,10 @@ struct FwdParams {
   int batch, n_q, n_k, h_q, h_kv, group;
   uint32_t k_bytes, v_bytes;  // byte extent of one (batch, kv head) slice of k / v
   uint32_t q_bytes;           // byte extent of one (batch, head) slice of q
+  // paged K/V (prefill over a paged cache): k and v are the caches
+  const int32_t* block_table;    // [batch][max_blocks_per_seq]
+  const int32_t* context_lens;   // [batch]: keys of each sequence
+  int max_blocks_per_seq;
   int n_qtiles;     // ceil(n_q / BM)
   int num_items;    // n_qtiles * batch * h_q
   int xcd_chunk;    // work items kept together on one XCD (0 = no remap)

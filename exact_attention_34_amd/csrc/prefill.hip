@@ -55,7 +55,10 @@ struct IntC {
   static constexpr int value = V;
 };
 
-template <typename TT, int D, bool CAUSAL>
+// PAGED: K and V are read from a paged KV cache ([blocks][h_kv][16][D])
+// through each sequence's block table, its context length sets n_k, and the
+// n_q query rows are the last n_q tokens of that context.
+template <typename TT, int D, bool CAUSAL, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(FwdParams p) {
   typedef typename TT::elem T;
@@ -99,19 +102,23 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const int qt = CAUSAL ? (p.n_qtiles - 1 - rank) : rank;
   const int q0 = qt * BM;
   const int kvh = h / p.group;
-  const int off = p.n_k - p.n_q;
+  // keys of this sequence
+  const int nk = PAGED ? __builtin_amdgcn_readfirstlane(p.context_lens[b]) : p.n_k;
+  const int off = nk - p.n_q;
 
-  int kend = p.n_k;
+  int kend = nk;
   if (CAUSAL) {
     const int qlast = min(q0 + BM, p.n_q) - 1;
-    kend = min(p.n_k, max(0, qlast + off + 1));
+    kend = min(nk, max(0, qlast + off + 1));
   }
   const int ntiles = (kend + BN - 1) / BN;
 
   const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const T* Kg = (const T*)p.k + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
-  const uint32_t krow = (uint32_t)p.ks_n * 2u, vrow = (uint32_t)p.vs_n * 2u;  // row pitch, bytes
+  // row pitch, bytes (paged: rows of one block of one KV head are contiguous)
+  const uint32_t krow = PAGED ? (uint32_t)D * 2u : (uint32_t)p.ks_n * 2u;
+  const uint32_t vrow = PAGED ? (uint32_t)D * 2u : (uint32_t)p.vs_n * 2u;
 
   // Q fragment (B operand of S^T = K Q^T): column = query, k = d.  Filled
   // in the prologue through LDS (see below).
@@ -143,13 +150,38 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   for (int i = 0; i < LOADS; ++i) {
     const int slot = (i * 4 + wave) * 64 + lane;
     const int row = slot / CPR, pc = slot % CPR;
-    kgo[i] = (uint32_t)row * krow + (uint32_t)((pc ^ kswz(row)) * 16);
-    vgo[i] = (uint32_t)row * vrow + (uint32_t)((pc ^ vswz(row)) * 16);
+    // paged: offsets within the row's 16-row block (tiles start on block edges)
+    const int brow = PAGED ? (row & 15) : row;
+    kgo[i] = (uint32_t)brow * krow + (uint32_t)((pc ^ kswz(row)) * 16);
+    vgo[i] = (uint32_t)brow * vrow + (uint32_t)((pc ^ vswz(row)) * 16);
   }
+  // Paged: the rows of one direct-load instruction (64 / CPR of them) lie in
+  // one 16-row block, so each instruction gets a resource based at its block
+  // of this KV head, whose extent stops at the context (later slots, and
+  // blocks past the last, read as zero).
+  const int nblk = (nk + 15) >> 4;
+  auto block_rsrc = [&](const void* cache, int kt, int ins) {
+    const int lb = (kt * BN + ins * (64 / CPR)) >> 4;
+    const char* base = (const char*)cache;
+    uint32_t ext = 0;
+    if (lb < nblk) {
+      const int64_t phys = p.block_table[(int64_t)b * p.max_blocks_per_seq + lb];
+      base += (phys * p.h_kv + kvh) * 16 * D * 2;
+      ext = (uint32_t)min(16, nk - lb * 16) * (uint32_t)D * 2u;
+    }
+    return make_rsrc(base, __builtin_amdgcn_readfirstlane(ext));
+  };
   // Per-lane offsets stay fixed; each tile gets a buffer resource based at its
   // first row (scalar arithmetic) whose extent is what is left of the slice,
   // so rows past n_k load as zero.
   auto load_k = [&](int kt, int stage) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        buf_load16_lds(block_rsrc(p.k, kt, i * 4 + wave), ks_lds + stage * TILE + (i * 4 + wave) * 512,
+                       kgo[i]);
+      return;
+    }
     const uint32_t o = (uint32_t)(kt * BN) * krow;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.k_bytes > o ? p.k_bytes - o : 0u);
     const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Kg + o, rem_b);
@@ -173,6 +205,13 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     }
   };
   auto load_v = [&](int kt, int stage) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        buf_load16_lds(block_rsrc(p.v, kt, i * 4 + wave), vs_lds + stage * TILE + (i * 4 + wave) * 512,
+                       vgo[i]);
+      return;
+    }
     const uint32_t o = (uint32_t)(kt * BN) * vrow;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.v_bytes > o ? p.v_bytes - o : 0u);
     const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Vg + o, rem_b);
@@ -209,7 +248,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   }
 
   // last key visible to this lane's query, clamped to the sequence
-  const int klast = CAUSAL ? min(qrow + off, p.n_k - 1) : p.n_k - 1;
+  const int klast = CAUSAL ? min(qrow + off, nk - 1) : nk - 1;
 
   if (ntiles > 0) {
     // ---- prologue: Q through LDS, K_0 and K_1 staged, the "previous" V
@@ -268,7 +307,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
           for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
       }
       const int k0 = kt * BN;
-      const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
+      const bool need_mask = (k0 + BN > nk) || (CAUSAL && (k0 + BN - 1 > q0 + off));
       if (need_mask) {
         // key of register r in half `sub`: k0 + hi*4 + sub*32 + (r/4)*8 + r%4
         const int lim = klast - (k0 + hi * 4);
@@ -528,7 +567,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
 // ----------------------------------------------------------------------------
 // host-side launchers
 // ----------------------------------------------------------------------------
-template <typename TT, int D, bool CAUSAL>
+template <typename TT, int D, bool CAUSAL, bool PAGED>
 static hipError_t launch_mfma(FwdParams p, hipStream_t stream) {
   constexpr int BM = 128;
   p.n_qtiles = (p.n_q + BM - 1) / BM;
@@ -538,12 +577,12 @@ static hipError_t launch_mfma(FwdParams p, hipStream_t stream) {
   p.k_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.ks_n + D) * 2) : 0u;
   p.v_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.vs_n + D) * 2) : 0u;
   p.q_bytes = p.n_q > 0 ? (uint32_t)(((int64_t)(p.n_q - 1) * p.qs_n + D) * 2) : 0u;
-  hipLaunchKernelGGL((attn_fwd_mfma_kernel<TT, D, CAUSAL>), dim3(p.num_items), dim3(256), 0,
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<TT, D, CAUSAL, PAGED>), dim3(p.num_items), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 static hipError_t launch_f32(FwdParams p, hipStream_t stream) {
   dim3 grid((p.n_q + 63) / 64, p.h_q, p.batch);
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, p);
@@ -553,15 +592,28 @@ static hipError_t launch_f32(FwdParams p, hipStream_t stream) {
 // dtype: 0 f32, 1 f16, 2 bf16.  Returns the launch status.
 hipError_t launch_prefill(int dtype, int head_dim, bool causal, const FwdParams& p,
                           hipStream_t stream) {
-#define ATTN_DISPATCH_D(FN, ...)                                          \
-  (head_dim == 64 ? (causal ? FN<__VA_ARGS__ 64, true>(p, stream)         \
-                            : FN<__VA_ARGS__ 64, false>(p, stream))       \
-                  : (causal ? FN<__VA_ARGS__ 128, true>(p, stream)        \
-                            : FN<__VA_ARGS__ 128, false>(p, stream)))
+#define ATTN_DISPATCH_D(FN, ...)                                                 \
+  (head_dim == 64 ? (causal ? FN<__VA_ARGS__ 64, true, false>(p, stream)         \
+                            : FN<__VA_ARGS__ 64, false, false>(p, stream))       \
+                  : (causal ? FN<__VA_ARGS__ 128, true, false>(p, stream)        \
+                            : FN<__VA_ARGS__ 128, false, false>(p, stream)))
   if (dtype == 2) return ATTN_DISPATCH_D(launch_mfma, BF16,);
   if (dtype == 1) return ATTN_DISPATCH_D(launch_mfma, F16,);
   return ATTN_DISPATCH_D(launch_f32, );
 #undef ATTN_DISPATCH_D
+}
+
+// Prefill over a paged KV cache (bf16 / fp16).
+hipError_t launch_prefill_paged(int dtype, int head_dim, bool causal, const FwdParams& p,
+                                hipStream_t stream) {
+#define ATTN_DISPATCH_P(TT)                                                    \
+  (head_dim == 64 ? (causal ? launch_mfma<TT, 64, true, true>(p, stream)       \
+                            : launch_mfma<TT, 64, false, true>(p, stream))     \
+                  : (causal ? launch_mfma<TT, 128, true, true>(p, stream)      \
+                            : launch_mfma<TT, 128, false, true>(p, stream)))
+  if (dtype == 2) return ATTN_DISPATCH_P(BF16);
+  return ATTN_DISPATCH_P(F16);
+#undef ATTN_DISPATCH_P
 }
 
 }  // namespace attn

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 /* element types of q, k, v, o and the KV cache */
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -296,6 +296,31 @@ int paged_attn_decode_shared(int dtype,
  * blocks shared by forked sequences and copied before a shared block is
  * written).
  */
+
+/*
+ * attn_fwd_paged -- prefill over a paged KV cache (chunked prefill): the n_q
+ * query rows of sequence b are the last n_q tokens of its context, whose
+ * K and V (already written, e.g. by paged_kv_write) are read through its
+ * block table.  Query row i sees keys j <= i + (context_lens[b] - n_q) when
+ * causal, all context_lens[b] keys otherwise; rows that see no key get o = 0
+ * and lse = -inf.  The result is attn_fwd's on the sequence's logical K/V.
+ *
+ *   q, o           [batch][n_q][h_q][head_dim] addressed by q_stride /
+ *                  o_stride (host arrays of 3, as attn_fwd).
+ *   k_cache, v_cache, block_table, block_size, num_blocks: as
+ *                  paged_attn_decode; context_lens device [batch], each in
+ *                  [0, max_context_len].
+ *   lse            optional [batch][h_q][n_q] fp32 (written).
+ *   dtype ATTN_F16 or ATTN_BF16; head_dim 64 or 128; the same kernel as
+ *   attn_fwd with K/V tile rows taken block by block.  Asynchronous.
+ */
+int attn_fwd_paged(int dtype, const void* q, const int64_t* q_stride,
+                   const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* context_lens,
+                   void* o, const int64_t* o_stride, float* lse,
+                   int batch, int n_q, int h_q, int h_kv, int head_dim, int block_size,
+                   int max_blocks_per_seq, int max_context_len, int num_blocks,
+                   float softmax_scale, int causal, void* stream);
 
 /*
  * paged_kv_write -- write the K and V rows of n_tokens new tokens into their

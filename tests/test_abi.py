@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ea.abi_version() == 5
+    assert ea.abi_version() == 6
 
 
 def test_workspace_size():
