@@ -17,6 +17,10 @@ Prints one JSON line:
   backward       outside the step: attn_bwd on the prefill workload (its own
                  O and log-sum-exp, a seeded dO), TFLOP/s counted as 2.5x the
                  forward's algorithmic FLOP, against the bf16 peak
+  paged_kv       outside the step: the prefill workload's K/V written into a
+                 paged cache (shuffled blocks) with paged_kv_write (GB/s), and
+                 the same prefill read back through the block table with
+                 attn_fwd_paged (TFLOP/s, beside the contiguous attn_fwd)
   cpu_baseline   the fp64 CPU oracle timed on the host on a bounded sample
 Kernel times come from HIP events recorded on the stream the kernels run on.
 
@@ -82,14 +86,16 @@ def parse():
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-prefix decode measurement (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward", "paged"],
+                    default=None,
                     help="run one kernel family only (for profiling)")
     ap.add_argument("--write-traffic", nargs="+", default=None, metavar="DIR")
     return ap.parse_args()
 
 
 TRAFFIC_KERNELS = {   # entry name -> (kernel name prefix in rocprofv3 output, run)
-    "attn_fwd_mfma_kernel": ("void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true>", "main"),
+    "attn_fwd_mfma_kernel": ("void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true, false>",
+                             "main"),
     "paged_decode_split_kernel": ("void attn::paged_decode_split_kernel<attn::BF16, 128, 4,",
                                   "main"),
     "paged_decode_combine_kernel": ("void attn::paged_decode_combine_kernel<attn::BF16", "main"),
@@ -299,6 +305,55 @@ def backward(ea, pre, q, k, v, pre_flops, reps):
     }
 
 
+def paged_kv(ea, pre, q, k, v, pre_flops, reps):
+    """paged_kv_write of the prefill workload's K and V into a shuffled paged
+    cache, then attn_fwd_paged over it; each timed over `reps` back-to-back
+    calls with HIP events on the current stream."""
+    B, N, Hq, d = q.shape
+    Hkv, bs = k.shape[2], 16
+    per_seq = (N + bs - 1) // bs
+    nb = B * per_seq
+    g = torch.Generator().manual_seed(11)
+    perm = torch.randperm(nb, generator=g).to(torch.int32)
+    table = perm.view(B, per_seq).to(q.device)
+    t = torch.arange(N, dtype=torch.int32)
+    slots = (perm.view(B, per_seq)[:, t // bs] * bs + t % bs).reshape(-1).to(q.device)
+    kc = torch.empty((nb, Hkv, bs, d), dtype=q.dtype, device=q.device)
+    vc = torch.empty_like(kc)
+    kf, vf = k.reshape(B * N, Hkv, d), v.reshape(B * N, Hkv, d)
+    ctx = torch.full((B,), N, dtype=torch.int32, device=q.device)
+    out = torch.empty_like(q)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_write = timed(lambda: ea.paged_kv_write(kf, vf, slots, kc, vc))
+    t_paged = timed(lambda: ea.attn_fwd_paged(q, kc, vc, table, ctx, max_context_len=N,
+                                              causal=True, scale=pre.scale, out=out))
+    t_flat = timed(lambda: ea.attn_fwd(q, k, v, causal=True, scale=pre.scale, out=out))
+    moved = 2 * 2 * kf.numel() * kf.element_size()   # K and V, read once and written once
+    return {
+        "workload": "prefill workload's K/V (B=4 x 2048 tokens, 16 KV heads, d=128, bf16) in "
+                    "%d shuffled 16-token blocks" % nb,
+        "kv_write_ms": t_write, "kv_write_GBps": moved / (t_write * 1e-3) / 1e9,
+        "kv_write_frac_of_hbm": moved / (t_write * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "paged_prefill_ms": t_paged,
+        "paged_prefill_TFLOPs": pre_flops / (t_paged * 1e-3) / 1e12,
+        "contiguous_prefill_ms": t_flat,
+        "contiguous_prefill_TFLOPs": pre_flops / (t_flat * 1e-3) / 1e12,
+        "note": "back-to-back calls on warm caches",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -329,6 +384,10 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps({"backward": backward(ea, pre, q, k, v, pre_flops, args.steps)}),
+              flush=True)
+        return
+    if args.only == "paged":
+        print(json.dumps({"paged_kv": paged_kv(ea, pre, q, k, v, pre_flops, args.steps)}),
               flush=True)
         return
 
@@ -412,6 +471,7 @@ def main():
     if args.only is None and not args.no_shared:
         res["shared_decode"] = shared_decode(ea, workloads, dev, args.steps)
         res["backward"] = backward(ea, pre, q, k, v, pre_flops, args.steps)
+        res["paged_kv"] = paged_kv(ea, pre, q, k, v, pre_flops, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre, dec, dec_bytes, pre_flops)
     print(json.dumps(res), flush=True)

@@ -86,6 +86,10 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   static_assert(32 % (NQK + NPV) == 0, "slot plan");
   __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * TILE];
+  // paged: this sequence's block table row, staged once so that the tile
+  // loads do not wait on table reads from memory
+  constexpr int kTabLds = PAGED ? 2048 : 1;
+  __shared__ __attribute__((aligned(16))) int32_t tab_lds[kTabLds < 4 ? 4 : kTabLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,13 +164,22 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   // of this KV head, whose extent stops at the context (later slots, and
   // blocks past the last, read as zero).
   const int nblk = (nk + 15) >> 4;
-  auto block_rsrc = [&](const void* cache, int kt, int ins) {
-    const int lb = (kt * BN + ins * (64 / CPR)) >> 4;
+  // The four blocks of tile kt are table entries 4 kt .. 4 kt + 3: one
+  // 16-byte read of the staged row (or of the table, past the staged part).
+  auto tile_blocks = [&](int kt) -> i32x4 {
+    const int lb0 = kt * (BN / 16);
+    if (lb0 + 4 <= kTabLds) return *(const i32x4*)(tab_lds + lb0);
+    i32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r[j] = lb0 + j < nblk ? p.block_table[(int64_t)b * p.max_blocks_per_seq + lb0 + j] : 0;
+    return r;
+  };
+  auto block_rsrc = [&](const void* cache, int lb, int phys) {
     const char* base = (const char*)cache;
     uint32_t ext = 0;
     if (lb < nblk) {
-      const int64_t phys = p.block_table[(int64_t)b * p.max_blocks_per_seq + lb];
-      base += (phys * p.h_kv + kvh) * 16 * D * 2;
+      base += ((int64_t)__builtin_amdgcn_readfirstlane(phys) * p.h_kv + kvh) * 16 * D * 2;
       ext = (uint32_t)min(16, nk - lb * 16) * (uint32_t)D * 2u;
     }
     return make_rsrc(base, __builtin_amdgcn_readfirstlane(ext));
@@ -176,10 +189,13 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   // so rows past n_k load as zero.
   auto load_k = [&](int kt, int stage) {
     if constexpr (PAGED) {
+      const i32x4 ids = tile_blocks(kt);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        buf_load16_lds(block_rsrc(p.k, kt, i * 4 + wave), ks_lds + stage * TILE + (i * 4 + wave) * 512,
-                       kgo[i]);
+      for (int i = 0; i < LOADS; ++i) {
+        const int j = (i * 4 + wave) * (64 / CPR) / 16;   // block of this instruction's rows
+        buf_load16_lds(block_rsrc(p.k, kt * (BN / 16) + j, ids[j]),
+                       ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
+      }
       return;
     }
     const uint32_t o = (uint32_t)(kt * BN) * krow;
@@ -206,10 +222,13 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   };
   auto load_v = [&](int kt, int stage) {
     if constexpr (PAGED) {
+      const i32x4 ids = tile_blocks(kt);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        buf_load16_lds(block_rsrc(p.v, kt, i * 4 + wave), vs_lds + stage * TILE + (i * 4 + wave) * 512,
-                       vgo[i]);
+      for (int i = 0; i < LOADS; ++i) {
+        const int j = (i * 4 + wave) * (64 / CPR) / 16;
+        buf_load16_lds(block_rsrc(p.v, kt * (BN / 16) + j, ids[j]),
+                       vs_lds + stage * TILE + (i * 4 + wave) * 512, vgo[i]);
+      }
       return;
     }
     const uint32_t o = (uint32_t)(kt * BN) * vrow;
@@ -251,6 +270,12 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const int klast = CAUSAL ? min(qrow + off, nk - 1) : nk - 1;
 
   if (ntiles > 0) {
+    if constexpr (PAGED) {
+      const int n = min(nblk, kTabLds);
+      for (int i = tid; i < n; i += 256)
+        tab_lds[i] = p.block_table[(int64_t)b * p.max_blocks_per_seq + i];
+      __syncthreads();
+    }
     // ---- prologue: Q through LDS, K_0 and K_1 staged, the "previous" V
     // stage zeroed, S_0 ----
     load_q(0);
