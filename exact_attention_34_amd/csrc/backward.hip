@@ -403,8 +403,14 @@ void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NS = D / 16;
   constexpr int TILE = BN * D;
   constexpr int LOADS = BN * CPR / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * TILE];
+  // one array per stage, so that the compiler can see that the stage being
+  // read is not the one the direct loads are filling
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds1[TILE];
+  auto kst = [&](int st) -> uint16_t* { return st ? ks_lds1 : ks_lds0; };
+  auto vst = [&](int st) -> uint16_t* { return st ? vs_lds1 : vs_lds0; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -467,24 +473,26 @@ void attn_bwd_dq_kernel(BwdParams p) {
   auto load_kv = [&](int kt, int stage) {
     const uint32_t ok = (uint32_t)(kt * BN) * krow, ov = (uint32_t)(kt * BN) * vrow;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(
-        (const char*)Kg + ok, __builtin_amdgcn_readfirstlane(p.k_bytes > ok ? p.k_bytes - ok : 0u));
+        uniform_ptr((const char*)Kg + ok),
+        __builtin_amdgcn_readfirstlane(p.k_bytes > ok ? p.k_bytes - ok : 0u));
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(
-        (const char*)Vg + ov, __builtin_amdgcn_readfirstlane(p.v_bytes > ov ? p.v_bytes - ov : 0u));
+        uniform_ptr((const char*)Vg + ov),
+        __builtin_amdgcn_readfirstlane(p.v_bytes > ov ? p.v_bytes - ov : 0u));
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      buf_load16_lds(rk, ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
-      buf_load16_lds(rv, vs_lds + stage * TILE + (i * 4 + wave) * 512, vgo[i]);
+      buf_load16_lds(rk, kst(stage) + (i * 4 + wave) * 512, kgo[i]);
+      buf_load16_lds(rv, vst(stage) + (i * 4 + wave) * 512, vgo[i]);
     }
   };
 
-  if (ntiles > 0) load_kv(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int S = kt & 1;
+  // one key tile, read from stage S (tile kt lands in stage kt & 1)
+  auto step = [&](const int kt, auto SC) {
+    constexpr int S = decltype(SC)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (kt + 1 < ntiles) load_kv(kt + 1, S ^ 1);
-    const uint16_t* kb = ks_lds + S * TILE;
-    const uint16_t* vb = vs_lds + S * TILE;
+    const uint16_t* kb = kst(S);
+    const uint16_t* vb = vst(S);
     const int k0 = kt * BN;
     const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
     // LDS read offsets, computed here rather than held across the loop
@@ -553,13 +561,20 @@ void attn_bwd_dq_kernel(BwdParams p) {
       dq[t] = TT::mma32(opnd[i], dsb[ks], dq[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  if (ntiles > 0) load_kv(0, 0);
+  int kt = 0;
+  for (; kt + 1 < ntiles; kt += 2) {
+    step(kt, IntC<0>());
+    step(kt + 1, IntC<1>());
   }
+  if (kt < ntiles) step(kt, IntC<0>());
 
   // ---- epilogue: dQ = scale dQ^T^T, whole rows through LDS ----
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  uint16_t* stage = (wave < 2 ? ks_lds : vs_lds) + (wave & 1) * 32 * (D + 8);
-  static_assert(2 * 32 * (D + 8) <= 2 * TILE, "output staging fits");
+  uint16_t* stage = wave < 2 ? kst(wave) : vst(wave - 2);
+  static_assert(32 * (D + 8) <= TILE, "a wave's output rows fit one stage");
   T* dQg = (T*)p.dq + (int64_t)b * p.dqs_b + (int64_t)h * p.dqs_h;
   store_rows<TT, D>(dq, p.scale, stage, lane, dQg, p.dqs_n, q0 + wave * 32, p.n_q);
 }

@@ -155,6 +155,20 @@ __device__ inline float pair_sum32(float x) {
 
 // Raw buffer resource over [base, base + bytes): loads whose byte offset
 // (the VGPR offset) is at or past `bytes` return zero.
+// A compile-time int as a type, for passing constants to generic lambdas.
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// A pointer that is the same in every lane, marked as such for the compiler
+// (a buffer resource must sit in scalar registers).
+__device__ inline const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
@@ -195,8 +209,9 @@ struct FwdParams {
   const int32_t* block_table;    // [batch][max_blocks_per_seq]
   const int32_t* context_lens;   // [batch]: keys of each sequence
   int max_blocks_per_seq;
-  int n_qtiles;     // ceil(n_q / BM)
-  int num_items;    // n_qtiles * batch * h_q
+  int hpw;          // query heads per workgroup (of one KV head's group)
+  int n_qtiles;     // ceil(n_q / rows per head of a workgroup)
+  int num_items;    // n_qtiles * batch * h_q / hpw
   int xcd_chunk;    // work items kept together on one XCD (0 = no remap)
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -271,5 +286,13 @@ struct SharedPlan {
   int n_rt, n_ch, chunk_blocks;
   int64_t items;   // workgroups of the prefix kernel
 };
+
+// Read-only metadata (context lengths, block tables) read through the
+// constant address space: at a wave-uniform index that is a scalar load, which
+// keeps the value in scalar registers and leaves the vector-memory counter to
+// the K/V loads.
+__device__ inline int ld_meta(const int32_t* ptr, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
+}
 
 }  // namespace attn

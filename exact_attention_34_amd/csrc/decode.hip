@@ -72,14 +72,6 @@ __device__ inline int wave_of(int64_t b, int64_t T, int W) {
   return w;
 }
 
-// Read-only metadata (context lengths, block table) is read through the
-// constant address space: at a wave-uniform index that is a scalar load, which
-// keeps the cursor in scalar registers and lets the vector-memory counter track
-// K/V loads only.
-__device__ inline int ld_meta(const int32_t* ptr, int64_t i) {
-  return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
-}
-
 // Total unit blocks over all sequences and those of sequences before `s`,
 // reduced across the 64 lanes of the calling wave (the results are uniform).
 __device__ inline void seq_block_sums(const DecodeParams& p, int s, int lane, int64_t& before,

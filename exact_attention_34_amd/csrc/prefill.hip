@@ -4,14 +4,18 @@
 // N x N score or probability matrix to device memory.
 //
 // 16-bit kernel (bf16 / fp16), gfx950 matrix cores:
-//   * a workgroup of 4 waves owns BM = 128 query rows of one (batch, head);
-//     each wave owns 32 rows, whose Q fragment stays in VGPRs for the whole
-//     kernel;
-//   * the loop walks the visible key range in BN = 64 tiles.  K tiles are
-//     copied to LDS as they are in memory ([key][d]); V tiles are transposed
-//     in registers on the way in and stored [d][key], so that both products
-//     read their operand with one 16-byte LDS load per lane.  Two LDS stages:
-//     tile j+1 is fetched from HBM into registers while tile j is computed;
+//   * a workgroup of 8 waves owns 256 query rows: 128 rows of each of two
+//     query heads that read the same KV head (GQA), or 256 rows of one head.
+//     Each wave owns 32 rows, whose Q fragment stays in VGPRs for the whole
+//     kernel.  Every K/V tile staged in LDS serves all 256 rows, which halves
+//     the L2-to-LDS traffic of a 128-row workgroup;
+//   * the loop walks the visible key range in BN = 64 tiles.  K and V tiles
+//     go from memory straight into LDS (buffer loads with the LDS bit), laid
+//     out [key][d] with 16-byte chunks permuted per row against bank
+//     conflicts; the K operand is one 16-byte LDS read per lane, the V
+//     operand two transposing 8-byte reads.  Two stages: tile j+1 lands while
+//     tile j is computed.  The stages are separate LDS arrays, so the
+//     compiler can see that a stage being read is not the one being filled;
 //   * scores are produced transposed, S^T = K Q^T (v_mfma_f32_32x32x16), so
 //     every lane holds one query column and 16 of its keys; the row max needs
 //     one exchange with lane l^32 and nothing else.  The same registers, once
@@ -22,9 +26,10 @@
 //     multiply; l is kept per lane and summed with lane l^32 at the end;
 //     O is divided by l once, in the epilogue;
 //   * causal: only the key tiles a workgroup can see are visited, the mask is
-//     applied only on tiles that cross the diagonal, and workgroups are issued
-//     longest first.  Work items that share K/V (the query heads of one GQA
-//     group) are kept together on one XCD.
+//     applied only on tiles that cross the diagonal, a wave stops computing
+//     once every later key is masked for all of its rows, and workgroups are
+//     issued longest first.  Work items that share K/V (the query heads of
+//     one GQA group) are kept together on one XCD.
 //
 // fp32 kernel: plain fp32 arithmetic on the vector ALUs (the fp32 matrix
 // rate equals the vector rate on this chip); four lanes share a query row.
@@ -50,22 +55,23 @@ __device__ inline int remap_item(int i, int num_items, int chunk) {
 // ----------------------------------------------------------------------------
 // 16-bit matrix-core kernel
 // ----------------------------------------------------------------------------
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-
 // PAGED: K and V are read from a paged KV cache ([blocks][h_kv][16][D])
 // through each sequence's block table, its context length sets n_k, and the
 // n_q query rows are the last n_q tokens of that context.
-template <typename TT, int D, bool CAUSAL, bool PAGED>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// NW waves per workgroup, 32 query rows each.  The workgroup's 32 NW rows
+// are p.hpw heads (of one KV head's group) x p.bm consecutive query rows; all
+// of them read the same K/V tiles, so each tile staged in LDS serves 32 NW
+// rows.
+template <typename TT, int D, bool CAUSAL, bool PAGED, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(FwdParams p) {
   typedef typename TT::elem T;
-  constexpr int BM = 128, BN = 64;
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int BN = 64;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TILE = BN * D;            // elements per K or V tile (no padding)
-  constexpr int LOADS = BN * CPR / 256;   // 16-byte direct loads per thread per tile
+  constexpr int LOADS = BN * CPR / NT;    // 16-byte direct loads per thread per tile
+  constexpr int QT = 32 * NW / BN;        // BN-row tiles of the workgroup's Q rows
   constexpr int NS = D / 16;              // k-steps of one S^T half (8 for d = 128)
   constexpr int NQK = 2 * NS;             // QK matrix ops per tile
   constexpr int NPV = (D / 32) * (BN / 16);  // PV matrix ops per tile
@@ -82,10 +88,21 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   // probabilities must stay in fp16 range, so there m is the maximum itself.
   constexpr float HEAD = TT::kIsBf16 ? 60.f : 0.f;
   constexpr float GROW = TT::kIsBf16 ? 40.f : 8.f;
-  static_assert(LOADS * 256 == BN * CPR, "tile split");
+  static_assert(LOADS * NT == BN * CPR, "tile split");
+  static_assert(QT == 2 || QT == 4, "Q staging");
   static_assert(32 % (NQK + NPV) == 0, "slot plan");
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2 * TILE];
+  // One array per stage: the tile loads write LDS directly, and the compiler
+  // only knows that a stage being read is not the one being filled when they
+  // are distinct objects (otherwise it waits for the loads before each read).
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_lds1[TILE];
+  auto kst = [&](int st) -> uint16_t* { return st ? ks_lds1 : ks_lds0; };
+  auto vst = [&](int st) -> uint16_t* { return st ? vs_lds1 : vs_lds0; };
+  // Q tiles 2 and 3 (eight waves) are staged here, tiles 0 and 1 in the V stages
+  __shared__ __attribute__((aligned(16))) uint16_t qx_lds[QT > 2 ? (QT - 2) * TILE : 8];
+  auto qst = [&](int t) -> uint16_t* { return t < 2 ? vst(t) : qx_lds + (t - 2) * TILE; };
   // paged: this sequence's block table row, staged once so that the tile
   // loads do not wait on table reads from memory
   constexpr int kTabLds = PAGED ? 2048 : 1;
@@ -98,26 +115,37 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const int hi = lane >> 5;    // which half of the k slots / key rows
 
   const int item = remap_item(blockIdx.x, p.num_items, p.xcd_chunk);
-  const int bh = p.batch * p.h_q;
+  const int hpw = p.hpw;                  // heads of this workgroup
+  const int bm = 32 * NW / hpw;           // query rows per head
+  const int wph = NW / hpw;               // waves per head
+  const int hgroups = p.h_q / hpw;
+  const int bh = p.batch * hgroups;
   const int rank = item / bh;
   const int rem = item - rank * bh;
-  const int b = rem / p.h_q;
-  const int h = rem - b * p.h_q;
+  const int b = rem / hgroups;
+  const int h0 = (rem - b * hgroups) * hpw;
   const int qt = CAUSAL ? (p.n_qtiles - 1 - rank) : rank;
-  const int q0 = qt * BM;
-  const int kvh = h / p.group;
+  const int q0 = qt * bm;
+  const int kvh = h0 / p.group;
+  // This wave's 32 rows are row block rb of the workgroup's list (head
+  // h0 + rb / wph, query rows q0 + 32 (rb % wph) ...).  The waves sharing a
+  // SIMD (w and w + NW/2) take blocks rb and NW - 1 - rb, so that under a
+  // causal mask each SIMD gets an equal share of the key tiles the waves
+  // skip.
+  const int rb = wave < NW / 2 ? wave : 3 * NW / 2 - 1 - wave;
+  const int h = h0 + rb / wph;
+  const int wr0 = q0 + (rb % wph) * 32;
   // keys of this sequence
   const int nk = PAGED ? __builtin_amdgcn_readfirstlane(p.context_lens[b]) : p.n_k;
   const int off = nk - p.n_q;
 
   int kend = nk;
   if (CAUSAL) {
-    const int qlast = min(q0 + BM, p.n_q) - 1;
+    const int qlast = min(q0 + bm, p.n_q) - 1;
     kend = min(nk, max(0, qlast + off + 1));
   }
   const int ntiles = (kend + BN - 1) / BN;
 
-  const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
   const T* Kg = (const T*)p.k + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const T* Vg = (const T*)p.v + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
   // row pitch, bytes (paged: rows of one block of one KV head are contiguous)
@@ -126,7 +154,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
 
   // Q fragment (B operand of S^T = K Q^T): column = query, k = d.  Filled
   // in the prologue through LDS (see below).
-  const int qrow = q0 + wave * 32 + col;
+  const int qrow = wr0 + col;
   u32x4 qf[NS];
 
   f32x16 oacc[D / 32];
@@ -152,7 +180,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   uint32_t kgo[LOADS], vgo[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int slot = (i * 4 + wave) * 64 + lane;
+    const int slot = (i * NW + wave) * 64 + lane;
     const int row = slot / CPR, pc = slot % CPR;
     // paged: offsets within the row's 16-row block (tiles start on block edges)
     const int brow = PAGED ? (row & 15) : row;
@@ -172,7 +200,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     i32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      r[j] = lb0 + j < nblk ? p.block_table[(int64_t)b * p.max_blocks_per_seq + lb0 + j] : 0;
+      r[j] = lb0 + j < nblk ? ld_meta(p.block_table, (int64_t)b * p.max_blocks_per_seq + lb0 + j) : 0;
     return r;
   };
   auto block_rsrc = [&](const void* cache, int lb, int phys) {
@@ -192,31 +220,35 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       const i32x4 ids = tile_blocks(kt);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int j = (i * 4 + wave) * (64 / CPR) / 16;   // block of this instruction's rows
+        // block of this instruction's rows (64 / CPR of them)
+        const int j = (i * NW + (wave & (NW - 1))) * (64 / CPR) / 16;
         buf_load16_lds(block_rsrc(p.k, kt * (BN / 16) + j, ids[j]),
-                       ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
+                       kst(stage) + (i * NW + wave) * 512, kgo[i]);
       }
       return;
     }
     const uint32_t o = (uint32_t)(kt * BN) * krow;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.k_bytes > o ? p.k_bytes - o : 0u);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Kg + o, rem_b);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr((const char*)Kg + o), rem_b);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, ks_lds + stage * TILE + (i * 4 + wave) * 512, kgo[i]);
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, kst(stage) + (i * NW + wave) * 512, kgo[i]);
   };
-  // The Q tile (BM = 2 BN rows) goes through the V stages, which are idle
-  // until the first tile: two BN-row tiles in the K layout, loaded the same
-  // coalesced way (rows past n_q read as zero).
+  // The workgroup's Q rows (QT tiles of BN rows, each of one head) go
+  // through the V stages, which are idle until the first tile, and qx_lds:
+  // in the K layout, loaded the same coalesced way (rows past n_q read as
+  // zero).
   const uint32_t qrowb = (uint32_t)p.qs_n * 2u;
   auto load_q = [&](int t) {
-    const uint32_t o = (uint32_t)(q0 + t * BN) * qrowb;
+    const int ht = h0 + (t * BN) / bm;
+    const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)ht * p.qs_h;
+    const uint32_t o = (uint32_t)(q0 + (t * BN) % bm) * qrowb;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.q_bytes > o ? p.q_bytes - o : 0u);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Qg + o, rem_b);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr((const char*)Qg + o), rem_b);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
+      const int slot = (i * NW + wave) * 64 + lane;
       const int row = slot / CPR, pc = slot % CPR;
-      buf_load16_lds(r, vs_lds + t * TILE + (i * 4 + wave) * 512,
+      buf_load16_lds(r, qst(t) + (i * NW + wave) * 512,
                      (uint32_t)row * qrowb + (uint32_t)((pc ^ kswz(row)) * 16));
     }
   };
@@ -225,17 +257,17 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       const i32x4 ids = tile_blocks(kt);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int j = (i * 4 + wave) * (64 / CPR) / 16;
+        const int j = (i * NW + (wave & (NW - 1))) * (64 / CPR) / 16;
         buf_load16_lds(block_rsrc(p.v, kt * (BN / 16) + j, ids[j]),
-                       vs_lds + stage * TILE + (i * 4 + wave) * 512, vgo[i]);
+                       vst(stage) + (i * NW + wave) * 512, vgo[i]);
       }
       return;
     }
     const uint32_t o = (uint32_t)(kt * BN) * vrow;
     const uint32_t rem_b = __builtin_amdgcn_readfirstlane(p.v_bytes > o ? p.v_bytes - o : 0u);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc((const char*)Vg + o, rem_b);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr((const char*)Vg + o), rem_b);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, vs_lds + stage * TILE + (i * 4 + wave) * 512, vgo[i]);
+    for (int i = 0; i < LOADS; ++i) buf_load16_lds(r, vst(stage) + (i * NW + wave) * 512, vgo[i]);
   };
   // Direct loads complete into LDS asynchronously: wait for them, then
   // barrier, before any wave reads the stage.
@@ -268,31 +300,40 @@ void attn_fwd_mfma_kernel(FwdParams p) {
 
   // last key visible to this lane's query, clamped to the sequence
   const int klast = CAUSAL ? min(qrow + off, nk - 1) : nk - 1;
+  // last key tile holding a key that one of this wave's rows sees (-1: none);
+  // the wave skips the products of later tiles (their probabilities are 0)
+  int last_w = wr0 < p.n_q ? ntiles - 1 : -1;
+  if (CAUSAL && last_w >= 0) {
+    const int kmax = min(min(wr0 + 31, p.n_q - 1) + off, nk - 1);
+    last_w = kmax < 0 ? -1 : min(last_w, kmax / BN);
+  }
+  last_w = __builtin_amdgcn_readfirstlane(last_w);   // uniform: the loop exits below are per wave
 
   if (ntiles > 0) {
     if constexpr (PAGED) {
       const int n = min(nblk, kTabLds);
-      for (int i = tid; i < n; i += 256)
+      for (int i = tid; i < n; i += NT)
         tab_lds[i] = p.block_table[(int64_t)b * p.max_blocks_per_seq + i];
       __syncthreads();
     }
     // ---- prologue: Q through LDS, K_0 and K_1 staged, the "previous" V
     // stage zeroed, S_0 ----
-    load_q(0);
-    load_q(1);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) load_q(t);
     load_k(0, 0);
     load_k(1, 1);
     wait_loads_and_sync();
     {
-      // this wave's 32 rows sit in Q tile wave / 2, rows 32 (wave % 2) + ...
-      const uint16_t* qb = vs_lds + (wave >> 1) * TILE + (wave & 1) * 32 * D;
+      // this wave's 32 rows sit in Q tile rb / 2, rows 32 (rb % 2) + ...
+      const uint16_t* qb = qst(rb >> 1) + (rb & 1) * 32 * D;
 #pragma unroll
       for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qb + kofs[s]);
     }
     __syncthreads();   // every wave holds its Q fragment before the V stages are reused
+    // the first tile's P V reads V stage 1 with P = 0: zero it (it held Q)
 #pragma unroll
-    for (int i = 0; i < TILE / 8 / 256; ++i)
-      *(u32x4*)(vs_lds + TILE + (tid + 256 * i) * 8) = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < TILE / 8 / NT; ++i)
+      *(u32x4*)(vs_lds1 + (tid + NT * i) * 8) = u32x4{0, 0, 0, 0};
     f32x16 st_cur[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -300,14 +341,14 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) st_cur[sub][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        st_cur[sub] = TT::mma32(*(const u32x4*)(ks_lds + sub * 32 * D + kofs[s]), qf[s], st_cur[sub]);
+        st_cur[sub] = TT::mma32(*(const u32x4*)(ks_lds0 + sub * 32 * D + kofs[s]), qf[s], st_cur[sub]);
     }
     float smax_cur = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) smax_cur = fmaxf(smax_cur, st_cur[sub][r]);
-    u32x4 pb_prev[4];
+    u32x4 pb_prev[4];   // P_{kt-1}, the B operand of its P V (0 before tile 1)
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb_prev[i] = u32x4{0, 0, 0, 0};
     float pend_alpha = 1.f;
@@ -359,8 +400,8 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       // ---- 32 slots: one matrix op each (S_{kt+1} then O += P_{kt-1}
       // V_{kt-1}), its LDS operand fetched PFD slots ahead, and a few vector
       // ops of the softmax of S_kt / the row max of S_{kt+1} ----
-      const uint16_t* kb = ks_lds + S * TILE;
-      const uint16_t* vb = vs_lds + S * TILE;
+      const uint16_t* kb = kst(S);
+      const uint16_t* vb = vst(S);
       auto fetch = [&](int i) -> u32x4 {
         if (i < NQK) return *(const u32x4*)(kb + (i / NS) * 32 * D + kofs[i % NS]);
         const int j = i - NQK, t = j / (BN / 16), ks = j % (BN / 16);
@@ -432,14 +473,28 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       smax_cur = smax_next;
     };
 
+    // A wave stops computing at tile last_w + 2: from tile last_w + 1 on
+    // every probability of its rows is 0, so S, P, l, O and the reference max
+    // stay as they are.  It still loads its share of the remaining tiles and
+    // joins their barriers.
     int kt = 0;
     for (; kt + 1 < ntiles; kt += 2) {
+      if (kt - 1 > last_w) break;
       tile(kt, IntC<1>());
+      if (kt > last_w) {
+        ++kt;
+        break;
+      }
       tile(kt + 1, IntC<0>());
     }
-    if (kt < ntiles) {
+    if (kt + 1 == ntiles && kt - 1 <= last_w) {
       tile(kt, IntC<1>());
       ++kt;
+    }
+    for (; kt < ntiles; ++kt) {   // tile kt fills stage kt & 1
+      wait_loads_and_sync();
+      load_k(kt + 2, kt & 1);
+      load_v(kt, kt & 1);
     }
     wait_loads_and_sync();
     // ---- the last P V (stage of tile ntiles - 1) ----
@@ -449,8 +504,8 @@ void attn_fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
     }
-    {
-      const uint16_t* vb = vs_lds + ((ntiles - 1) & 1) * TILE;
+    if (ntiles - 1 <= last_w) {
+      const uint16_t* vb = vst((ntiles - 1) & 1);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -469,13 +524,15 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   const float l_tot = pair_sum32(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   {
-    // Each wave's 32 output rows go through LDS (rows padded by 16 bytes
-    // against bank conflicts) so that each store instruction writes four
-    // whole rows instead of 8-byte pieces of 32 rows.
-    constexpr int OP = D + 8;   // padded row, elements
-    static_assert(4 * 32 * OP <= 4 * TILE, "O staging fits the K and V stages");
+    // Each wave's 32 output rows go through LDS (16-byte chunk c of row r
+    // at c ^ (r % CPR), against bank conflicts) so that each store
+    // instruction writes whole rows instead of 8-byte pieces of 32 rows.  Two
+    // waves share each K or V stage.
+    static_assert(NW <= 8 && 64 * D <= TILE, "O staging fits the K and V stages");
     __syncthreads();            // every wave is done with the K/V stages
-    uint16_t* ow = (wave < 2 ? ks_lds : vs_lds) + (wave & 1) * 32 * OP;
+    uint16_t* ow = ((wave >> 1) & 3) < 2 ? kst(wave >> 1) : vst((wave >> 1) - 2);
+    ow += (wave & 1) * 32 * D;
+    auto oswz = [](int r) { return r & (CPR - 1); };
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -483,7 +540,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
         u32x2 w;
         w.x = TT::pack2(oacc[t][4 * g + 0] * inv, oacc[t][4 * g + 1] * inv);
         w.y = TT::pack2(oacc[t][4 * g + 2] * inv, oacc[t][4 * g + 3] * inv);
-        *(u32x2*)(ow + col * OP + t * 32 + g * 8 + hi * 4) = w;
+        *(u32x2*)(ow + col * D + (((4 * t + g) ^ oswz(col)) * 8) + hi * 4) = w;
       }
     lds_order();
     // lane l: chunk l % CPR of row (l / CPR) + (64 / CPR) i of this wave's rows
@@ -492,8 +549,8 @@ void attn_fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = i * RPI + lane / CPR;
-      const int grow = q0 + wave * 32 + r;
-      const u32x4 v = *(const u32x4*)(ow + r * OP + (lane % CPR) * 8);
+      const int grow = wr0 + r;
+      const u32x4 v = *(const u32x4*)(ow + r * D + (((lane % CPR) ^ oswz(r)) * 8));
       if (grow < p.n_q) *(u32x4*)(Ob + (int64_t)grow * p.os_n + (lane % CPR) * 8) = v;
     }
   }
@@ -594,16 +651,20 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
 // ----------------------------------------------------------------------------
 template <typename TT, int D, bool CAUSAL, bool PAGED>
 static hipError_t launch_mfma(FwdParams p, hipStream_t stream) {
-  constexpr int BM = 128;
-  p.n_qtiles = (p.n_q + BM - 1) / BM;
-  p.num_items = p.n_qtiles * p.batch * p.h_q;
-  p.xcd_chunk = p.group > 1 ? p.group : 1;
+  constexpr int NW = 8;   // waves per workgroup: 256 query rows share each K/V tile
+  // two heads of one KV head's group per workgroup when the group allows,
+  // else 256 rows of one head
+  p.hpw = (p.group % 2 == 0) ? 2 : 1;
+  const int bm = 32 * NW / p.hpw;
+  p.n_qtiles = (p.n_q + bm - 1) / bm;
+  p.num_items = p.n_qtiles * p.batch * (p.h_q / p.hpw);
+  p.xcd_chunk = p.group / p.hpw > 1 ? p.group / p.hpw : 1;
   // bytes from the first row of a (batch, kv head) slice to the end of its last row
   p.k_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.ks_n + D) * 2) : 0u;
   p.v_bytes = p.n_k > 0 ? (uint32_t)(((int64_t)(p.n_k - 1) * p.vs_n + D) * 2) : 0u;
   p.q_bytes = p.n_q > 0 ? (uint32_t)(((int64_t)(p.n_q - 1) * p.qs_n + D) * 2) : 0u;
-  hipLaunchKernelGGL((attn_fwd_mfma_kernel<TT, D, CAUSAL, PAGED>), dim3(p.num_items), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<TT, D, CAUSAL, PAGED, NW>), dim3(p.num_items),
+                     dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
