@@ -94,7 +94,7 @@ def parse():
 
 
 TRAFFIC_KERNELS = {   # entry name -> (kernel name prefix in rocprofv3 output, run)
-    "attn_fwd_mfma_kernel": ("void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true, false>",
+    "attn_fwd_mfma_kernel": ("void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true, false, 8>",
                              "main"),
     "paged_decode_split_kernel": ("void attn::paged_decode_split_kernel<attn::BF16, 128, 4,",
                                   "main"),

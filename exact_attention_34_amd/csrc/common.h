@@ -176,6 +176,11 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// The same with the non-temporal hint (cache policy bit 1): data read once
+// and streamed past.
+__device__ inline u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
 // 16 bytes per lane straight from memory into LDS: the wave's 64 lanes fill
 // 1 KiB of consecutive LDS starting at `lds` (a wave-uniform address), lane i
 // at lds + 16 i.  Completion is tracked by vmcnt.

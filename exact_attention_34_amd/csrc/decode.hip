@@ -221,7 +221,9 @@ void paged_decode_split_kernel(DecodeParams p) {
 
   u32x4 kr[RING][KST], vr[RING][VST];
   // Loads of one (block, KV head) tile through buffer resources based at the
-  // tile (scalar base, every lane offset inside it).  A refill past the end of
+  // tile (scalar base, every lane offset inside it), marked non-temporal: each
+  // K/V byte is read once, and streaming it past the caches keeps them for
+  // the data that is reused.  A refill past the end of
   // the range uses an empty resource: the loads still issue, in the same
   // order, but return zeros without touching memory.
   auto issue = [&](const Cursor& cu, int slot, bool real) {
@@ -236,10 +238,10 @@ void paged_decode_split_kernel(DecodeParams p) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, real ? (uint32_t)blk_bytes : 0u);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, real ? (uint32_t)blk_bytes : 0u);
 #pragma unroll
-    for (int st = 0; st < KST; ++st) kr[slot][st] = buf_load16(rk, kl + st * 64);
+    for (int st = 0; st < KST; ++st) kr[slot][st] = buf_load16_nt(rk, kl + st * 64);
 #pragma unroll
     for (int st = 0; st < VST; ++st)
-      vr[slot][st] = buf_load16(rv, vl + ((st & 1) + (st >> 1) * 2 * ROWS) * D * 2);
+      vr[slot][st] = buf_load16_nt(rv, vl + ((st & 1) + (st >> 1) * 2 * ROWS) * D * 2);
   };
   // query heads of a unit as the A operand of S = Q K^T (rows = heads, zero padded)
   u32x4 qa[KST];

@@ -551,7 +551,10 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       const int r = i * RPI + lane / CPR;
       const int grow = wr0 + r;
       const u32x4 v = *(const u32x4*)(ow + r * D + (((lane % CPR) ^ oswz(r)) * 8));
-      if (grow < p.n_q) *(u32x4*)(Ob + (int64_t)grow * p.os_n + (lane % CPR) * 8) = v;
+      // non-temporal: O is not read back here, and lines it leaves dirty in
+      // the caches would be written back during whatever kernel runs next
+      if (grow < p.n_q)
+        __builtin_nontemporal_store(v, (u32x4*)(Ob + (int64_t)grow * p.os_n + (lane % CPR) * 8));
     }
   }
   if (qrow < p.n_q) {

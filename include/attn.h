@@ -210,6 +210,10 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int h_kv, int hea
  * writes the empty-context outputs).  Results do not depend on which
  * physical blocks hold the data: the same logical sequences give bit-identical
  * outputs under any block table.  num_seqs == 0 is a no-op.
+ * K and V are read with the non-temporal cache hint (each byte once, streamed
+ * past the caches): a block that several rows of the table share is fetched
+ * from memory again for each.  Batches whose sequences share prefix blocks
+ * are served better by paged_attn_decode_shared, which reads them once.
  */
 int paged_attn_decode(int dtype,
                       const void* q, const void* k_cache, const void* v_cache,
