@@ -104,6 +104,8 @@ SHAPES = [
     (1, 257, 190, 8, 8, 64, "f16", False),
     (1, 640, 640, 16, 2, 128, "f16", True),
     (1, 384, 384, 8, 1, 128, "bf16", True),     # GQA 8:1
+    (2, 300, 300, 3, 1, 128, "bf16", True),     # odd group: 256 rows of one head per workgroup
+    (1, 600, 250, 6, 2, 128, "bf16", True),     # odd group, Nq > Nk: whole waves see no key
     (2, 96, 96, 3, 1, 128, "f32", True),
     (1, 200, 77, 2, 2, 64, "f32", False),
     (1, 513, 513, 2, 1, 128, "f32", True),
