@@ -35,26 +35,42 @@ namespace attn {
 // ----------------------------------------------------------------------------
 // delta = rowsum(dO * O)
 // ----------------------------------------------------------------------------
+// Rows are taken in (position, head) order, so that with the usual
+// [batch][position][head][d] layout a workgroup reads one contiguous stretch.
 template <typename TT, int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   typedef typename TT::elem T;
   constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int RPB = 256 / CPR;   // rows per workgroup
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x * RPB + tid / CPR, c = tid % CPR;
-  const int h = blockIdx.y, b = blockIdx.z;
-  float acc = 0.f;
-  if (row < p.n_q) {
-    const u32x4 o = *(const u32x4*)((const T*)p.o + (int64_t)b * p.os_b + (int64_t)row * p.os_n +
-                                    (int64_t)h * p.os_h + c * 8);
-    const u32x4 g = *(const u32x4*)((const T*)p.dout + (int64_t)b * p.dos_b +
-                                    (int64_t)row * p.dos_n + (int64_t)h * p.dos_h + c * 8);
+  constexpr int RPP = 256 / CPR;   // rows per pass of the workgroup
+  constexpr int PASSES = 4;        // rows of a thread, loaded together
+  const int tid = threadIdx.x, c = tid % CPR;
+  const int b = blockIdx.y;
+  const int64_t nrows = (int64_t)p.n_q * p.h_q;
+  const T* Ob = (const T*)p.o + (int64_t)b * p.os_b + c * 8;
+  const T* Gb = (const T*)p.dout + (int64_t)b * p.dos_b + c * 8;
+  u32x4 o[PASSES], g[PASSES];
+  int n[PASSES], h[PASSES];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc = TT::dot2(o[k], g[k], acc);
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = ((int64_t)blockIdx.x * PASSES + i) * RPP + tid / CPR;
+    n[i] = (int)(r / p.h_q);
+    h[i] = (int)(r - (int64_t)n[i] * p.h_q);
+    o[i] = g[i] = u32x4{0, 0, 0, 0};
+    if (r < nrows) {
+      o[i] = *(const u32x4*)(Ob + (int64_t)n[i] * p.os_n + (int64_t)h[i] * p.os_h);
+      g[i] = *(const u32x4*)(Gb + (int64_t)n[i] * p.dos_n + (int64_t)h[i] * p.dos_h);
+    }
   }
 #pragma unroll
-  for (int sh = 1; sh < CPR; sh <<= 1) acc += __shfl_xor(acc, sh);
-  if (c == 0 && row < p.n_q) p.delta[((int64_t)b * p.h_q + h) * p.n_q + row] = acc;
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = ((int64_t)blockIdx.x * PASSES + i) * RPP + tid / CPR;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = TT::dot2(o[i][k], g[i][k], acc);
+#pragma unroll
+    for (int sh = 1; sh < CPR; sh <<= 1) acc += __shfl_xor(acc, sh);
+    if (c == 0 && r < nrows) p.delta[((int64_t)b * p.h_q + h[i]) * p.n_q + n[i]] = acc;
+  }
 }
 
 // LDS tiles of these kernels are row-major [row][d] with 16-byte chunk c of
@@ -584,15 +600,16 @@ void attn_bwd_dq_kernel(BwdParams p) {
 // ----------------------------------------------------------------------------
 template <typename TT, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int RPB = 4 * 256 / (D / 8);   // rows per delta workgroup
   p.n_qt = (p.n_q + 127) / 128;
   p.n_kt = (p.n_k + 127) / 128;
   // with no query rows dK = dV = 0; with no keys dQ = 0 (the kernels write
   // the zeros); empty grids are not launched
   hipError_t e = hipSuccess;
   if (p.n_q > 0) {
-    hipLaunchKernelGGL((attn_bwd_delta_kernel<TT, D>),
-                       dim3((p.n_q + RPB - 1) / RPB, p.h_q, p.batch), dim3(256), 0, stream, p);
+    const int64_t rows = (int64_t)p.n_q * p.h_q;
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<TT, D>), dim3((unsigned)((rows + RPB - 1) / RPB), p.batch),
+                       dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.n_k > 0) {
