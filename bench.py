@@ -255,8 +255,10 @@ def shared_decode(ea, workloads, dev, reps):
         "shared_logical_GBps": logical / (t_shared * 1e-3) / 1e9,
         "shared_unique_GBps": unique / (t_shared * 1e-3) / 1e9,
         "shared_unique_frac_of_hbm": unique / (t_shared * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "note": "back-to-back calls: the 201 MB of unique K/V largely stays in the 256 MB "
-                "last-level cache between calls",
+        "note": "back-to-back calls.  The per-sequence call streams K/V past the caches "
+                "(non-temporal loads), so each sequence fetches the shared prefix again; the "
+                "sharing-aware call reads each prefix block once, with ordinary loads that can "
+                "hit the 256 MB last-level cache between calls",
         "prefix_kernel_traffic": load_traffic("paged_decode_prefix_kernel"),
     }
 
