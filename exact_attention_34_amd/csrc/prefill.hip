@@ -316,8 +316,7 @@ void attn_fwd_mfma_kernel(FwdParams p) {
         tab_lds[i] = p.block_table[(int64_t)b * p.max_blocks_per_seq + i];
       __syncthreads();
     }
-    // ---- prologue: Q through LDS, K_0 and K_1 staged, the "previous" V
-    // stage zeroed, S_0 ----
+    // ---- prologue: Q through LDS, K_0 and K_1 staged, S_0 ----
 #pragma unroll
     for (int t = 0; t < QT; ++t) load_q(t);
     load_k(0, 0);
@@ -329,11 +328,6 @@ void attn_fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qb + kofs[s]);
     }
-    __syncthreads();   // every wave holds its Q fragment before the V stages are reused
-    // the first tile's P V reads V stage 1 with P = 0: zero it (it held Q)
-#pragma unroll
-    for (int i = 0; i < TILE / 8 / NT; ++i)
-      *(u32x4*)(vs_lds1 + (tid + NT * i) * 8) = u32x4{0, 0, 0, 0};
     f32x16 st_cur[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -348,16 +342,21 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) smax_cur = fmaxf(smax_cur, st_cur[sub][r]);
-    u32x4 pb_prev[4];   // P_{kt-1}, the B operand of its P V (0 before tile 1)
+    u32x4 pb_prev[4];   // P_{kt-1}, the B operand of its P V
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb_prev[i] = u32x4{0, 0, 0, 0};
     float pend_alpha = 1.f;
     bool pend_grow = false;
-    __syncthreads();   // every wave is done with K stage 0 before it is refilled
+    // every wave holds its Q fragment (read from the V stages) and is done
+    // with K stage 0 before tile 0 refills them
+    __syncthreads();
 
-    // One tile.  Reads stage S (K_{kt+1}, V_{kt-1}); loads go to stage S ^ 1.
-    auto tile = [&](const int kt, auto SC) {
+    // One tile: the softmax of S_kt, S_{kt+1} = K_{kt+1} Q^T and its row
+    // max, and (PV) O += P_{kt-1} V_{kt-1}; tile 0 has no P V.  Reads stage
+    // S (K_{kt+1}, V_{kt-1}); loads go to stage S ^ 1.
+    auto tile = [&](const int kt, auto SC, auto PVC) {
       constexpr int S = decltype(SC)::value;
+      constexpr bool PV = decltype(PVC)::value != 0;
       // all waves are done with the stage refilled below, and the tiles
       // loaded last time have landed
       if (kt > 0) wait_loads_and_sync();
@@ -366,40 +365,44 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       load_k(kt + 2, S ^ 1);
       load_v(kt, S ^ 1);
       // O holds P_{kt-2} V_{kt-2}: move it to the reference of tile kt-1
-      if (pend_grow) {
+      if (PV && pend_grow) {
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
       }
-      const int k0 = kt * BN;
-      const bool need_mask = (k0 + BN > nk) || (CAUSAL && (k0 + BN - 1 > q0 + off));
-      if (need_mask) {
-        // key of register r in half `sub`: k0 + hi*4 + sub*32 + (r/4)*8 + r%4
-        const int lim = klast - (k0 + hi * 4);
-        smax_cur = -INFINITY;
+      float alpha, neg_m;
+      bool grow;
+      {
+        const int k0 = kt * BN;
+        const bool need_mask = (k0 + BN > nk) || (CAUSAL && (k0 + BN - 1 > q0 + off));
+        if (need_mask) {
+          // key of register r in half `sub`: k0 + hi*4 + sub*32 + (r/4)*8 + r%4
+          const int lim = klast - (k0 + hi * 4);
+          smax_cur = -INFINITY;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+          for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rel = sub * 32 + (r >> 2) * 8 + (r & 3);
-            st_cur[sub][r] = (rel <= lim) ? st_cur[sub][r] : -INFINITY;
-            smax_cur = fmaxf(smax_cur, st_cur[sub][r]);
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int rel = sub * 32 + (r >> 2) * 8 + (r & 3);
+              st_cur[sub][r] = (rel <= lim) ? st_cur[sub][r] : -INFINITY;
+              smax_cur = fmaxf(smax_cur, st_cur[sub][r]);
+            }
+        }
+        const float tmax = pair_max32(smax_cur) * c;
+        grow = tmax > m_run + GROW;
+        // lanes that do not grow keep their reference (alpha = 1, which also
+        // covers rows that have not seen a visible key, m = -inf); a row
+        // leaving -inf gets alpha = 0
+        const float m_new = tmax + HEAD;
+        alpha = fast_exp2(grow ? m_run - m_new : 0.f);
+        m_run = grow ? m_new : m_run;
+        neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       }
-      const float tmax = pair_max32(smax_cur) * c;
-      const bool grow = tmax > m_run + GROW;
-      // lanes that do not grow keep their reference (alpha = 1, which also
-      // covers rows that have not seen a visible key, m = -inf); a row
-      // leaving -inf gets alpha = 0
-      const float m_new = tmax + HEAD;
-      const float alpha = fast_exp2(grow ? m_run - m_new : 0.f);
-      m_run = grow ? m_new : m_run;
-      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
-      // ---- 32 slots: one matrix op each (S_{kt+1} then O += P_{kt-1}
-      // V_{kt-1}), its LDS operand fetched PFD slots ahead, and a few vector
-      // ops of the softmax of S_kt / the row max of S_{kt+1} ----
+      // ---- the slots: one matrix op each (S_{kt+1} then O += P_{kt-1}
+      // V_{kt-1}), its LDS operand fetched PFD slots ahead, and a share of
+      // the vector ops of the softmax of S_kt / the row max of S_{kt+1} ----
       const uint16_t* kb = kst(S);
       const uint16_t* vb = vst(S);
       auto fetch = [&](int i) -> u32x4 {
@@ -413,15 +416,35 @@ void attn_fwd_mfma_kernel(FwdParams p) {
         return u32x4{lo.x, lo.y, hi8.x, hi8.y};
       };
       constexpr int NSLOT = NQK + NPV;
+      // slots that issue a matrix op: [0, NA)
+      constexpr int NA = PV ? NSLOT : NQK;
       f32x16 st_next[2];
       u32x4 pb_cur[4];
       float psum = 0.f, pe_prev = 0.f, smax_next = -INFINITY;
+      // softmax of S_kt, probability e (32 per lane), packed in pairs
+      auto softmax_elem = [&](int e) {
+        const int sub = e / 16, r = e % 16;
+        // the empty volatile statements keep this slot's vector work
+        // between this slot's neighbours in the instruction stream
+        float x = st_cur[sub][r];
+        asm volatile("" : "+v"(x));
+        float pe = fast_exp2(fmaf(x, c, neg_m));
+        asm volatile("" : "+v"(pe));
+        if (r & 1) {
+          const uint32_t w = TT::pack2(pe_prev, pe);
+          // l sums the rounded values that enter P V, so the normalisation
+          // matches the weights actually applied
+          psum = TT::sum2(w, psum);
+          pb_cur[sub * 2 + (r >> 3)][(r & 7) >> 1] = w;
+        }
+        pe_prev = pe;
+      };
       u32x4 opnd[NSLOT];
 #pragma unroll
       for (int i = 0; i < PFD; ++i) opnd[i] = fetch(i);
 #pragma unroll
-      for (int i = 0; i < NSLOT; ++i) {
-        if (i + PFD < NSLOT) opnd[i + PFD] = fetch(i + PFD);
+      for (int i = 0; i < NA; ++i) {
+        if (i + PFD < NA) opnd[i + PFD] = fetch(i + PFD);
         if (i < NQK) {
           const int sub = i / NS, s = i % NS;
           if (s == 0) {
@@ -433,26 +456,8 @@ void attn_fwd_mfma_kernel(FwdParams p) {
           const int j = i - NQK, t = j / (BN / 16), ks = j % (BN / 16);
           oacc[t] = TT::mma32(opnd[i], pb_prev[ks], oacc[t]);
         }
-        // softmax of S_kt: 32 probabilities per lane spread over the slots,
-        // packed in pairs
 #pragma unroll
-        for (int e = i * 32 / NSLOT; e < (i + 1) * 32 / NSLOT; ++e) {
-          const int sub = e / 16, r = e % 16;
-          // the empty volatile statements keep this slot's vector work
-          // between this slot's neighbours in the instruction stream
-          float x = st_cur[sub][r];
-          asm volatile("" : "+v"(x));
-          float pe = fast_exp2(fmaf(x, c, neg_m));
-          asm volatile("" : "+v"(pe));
-          if (r & 1) {
-            const uint32_t w = TT::pack2(pe_prev, pe);
-            // l sums the rounded values that enter P V, so the normalisation
-            // matches the weights actually applied
-            psum = TT::sum2(w, psum);
-            pb_cur[sub * 2 + (r >> 3)][(r & 7) >> 1] = w;
-          }
-          pe_prev = pe;
-        }
+        for (int e = i * 32 / NA; e < (i + 1) * 32 / NA; ++e) softmax_elem(e);
         // row max of S_{kt+1}, once its products have landed
         if (i >= NQK) {
           const int j = i - NQK;                 // 0..NPV-1
@@ -463,6 +468,10 @@ void attn_fwd_mfma_kernel(FwdParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (!PV) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) smax_next = fmaxf(smax_next, st_next[e / 16][e % 16]);
+      }
       l_run = l_run * alpha + psum;
       pend_alpha = alpha;
       pend_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
@@ -472,40 +481,17 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       for (int sub = 0; sub < 2; ++sub) st_cur[sub] = st_next[sub];
       smax_cur = smax_next;
     };
-
-    // A wave stops computing at tile last_w + 2: from tile last_w + 1 on
-    // every probability of its rows is 0, so S, P, l, O and the reference max
-    // stay as they are.  It still loads its share of the remaining tiles and
-    // joins their barriers.
-    int kt = 0;
-    for (; kt + 1 < ntiles; kt += 2) {
-      if (kt - 1 > last_w) break;
-      tile(kt, IntC<1>());
-      if (kt > last_w) {
-        ++kt;
-        break;
+    using T1 = IntC<1>;
+    using T0 = IntC<0>;
+    // the wave's last P V, O += P_L V_L, from the V stage of tile L
+    auto last_pv = [&](int L) {
+      if (pend_grow) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
       }
-      tile(kt + 1, IntC<0>());
-    }
-    if (kt + 1 == ntiles && kt - 1 <= last_w) {
-      tile(kt, IntC<1>());
-      ++kt;
-    }
-    for (; kt < ntiles; ++kt) {   // tile kt fills stage kt & 1
-      wait_loads_and_sync();
-      load_k(kt + 2, kt & 1);
-      load_v(kt, kt & 1);
-    }
-    wait_loads_and_sync();
-    // ---- the last P V (stage of tile ntiles - 1) ----
-    if (pend_grow) {
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] *= pend_alpha;
-    }
-    if (ntiles - 1 <= last_w) {
-      const uint16_t* vb = vst((ntiles - 1) & 1);
+      const uint16_t* vb = vst(L & 1);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -517,7 +503,37 @@ void attn_fwd_mfma_kernel(FwdParams p) {
               (__attribute__((address_space(3))) i16x4*)(a + 8 * D)));
           oacc[t] = TT::mma32(u32x4{lo.x, lo.y, hi8.x, hi8.y}, pb_prev[ks], oacc[t]);
         }
+    };
+
+    // The wave computes tiles 0 .. L = last_w (tile 0 has no P V).  Its
+    // last P V, P_L V_L, comes in tile L + 1, before that tile's loads are
+    // issued (so no load into LDS is in flight while it reads V_L), or after
+    // the loop when L is the last tile.  From then on the wave only issues
+    // its share of the remaining tile loads and joins their barriers.  Tile
+    // kt reads stage (kt & 1) ^ 1.
+    const int L = last_w;
+    int kt = 0;
+    if (L >= 0) {
+      tile(0, T1(), T0());
+      for (kt = 1; kt + 1 <= L; kt += 2) {
+        tile(kt, T0(), T1());
+        tile(kt + 1, T1(), T1());
+      }
+      if (kt <= L) {
+        tile(kt, T0(), T1());
+        ++kt;
+      }
     }
+    // (a wave with no visible key starts here at tile 0, which, as for the
+    // others, has no barrier: every wave passes the same barriers)
+    for (; kt < ntiles; ++kt) {   // tile kt fills stage kt & 1
+      if (kt > 0) wait_loads_and_sync();
+      if (L >= 0 && kt == L + 1) last_pv(L);
+      load_k(kt + 2, kt & 1);
+      load_v(kt, kt & 1);
+    }
+    wait_loads_and_sync();
+    if (L >= 0 && L == ntiles - 1) last_pv(L);
   }
 
   // ---- epilogue: O = O^T / l, LSE ----
