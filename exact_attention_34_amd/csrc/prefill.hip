@@ -431,10 +431,15 @@ void attn_fwd_mfma_kernel(FwdParams p) {
         float pe = fast_exp2(fmaf(x, c, neg_m));
         asm volatile("" : "+v"(pe));
         if (r & 1) {
-          const uint32_t w = TT::pack2(pe_prev, pe);
+          // (pinned here too: otherwise the compiler sinks the packs and the
+          // dependent chain of sums to the top of the next tile, where no
+          // matrix op runs beside them)
+          uint32_t w = TT::pack2(pe_prev, pe);
+          asm volatile("" : "+v"(w));
           // l sums the rounded values that enter P V, so the normalisation
           // matches the weights actually applied
           psum = TT::sum2(w, psum);
+          asm volatile("" : "+v"(psum));
           pb_cur[sub * 2 + (r >> 3)][(r & 7) >> 1] = w;
         }
         pe_prev = pe;
