@@ -74,12 +74,22 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 }
 
 // LDS tiles of these kernels are row-major [row][d] with 16-byte chunk c of
-// row r stored at c ^ (r % 16), filled by direct buffer -> LDS loads (each
-// lane fetches the global chunk that belongs in its LDS slot).  Row reads (16
-// bytes of one row per lane, 32 rows) then hit distinct banks.
+// row r stored at c ^ tswz(r), filled by direct buffer -> LDS loads (each lane
+// fetches the global chunk that belongs in its LDS slot).  The tiles are read
+// two ways, and the permutation keeps both free of bank conflicts:
+//   * row reads: 16 bytes of one row per lane, one chunk of 32 consecutive
+//     rows; tswz is a bijection on r % 16 (d = 128), or on the rows of one
+//     parity within 16 (d = 64, two 128-byte rows per 256 bytes of banks);
+//   * transposing reads (below): 32 lanes read 4 consecutive rows (4k ..
+//     4k + 3) x 4 consecutive chunks (4t .. 4t + 3); the bits of tswz above
+//     the low two differ between those rows, so the 16 chunks land in
+//     distinct banks.
+// d = 128: tswz(r) = 4 (r % 4) + (r / 4) % 4 (a rotation of r % 16).
+// d = 64:  tswz(r) = 4 ((r / 2) % 2) + (r / 4) % 4.
 template <int CPR>
 __device__ inline int tswz(int r) {
-  return (r & 15) & (CPR - 1);
+  if (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Per-lane offsets (elements) of the transposing reads of a 32-column block t
@@ -87,8 +97,8 @@ __device__ inline int tswz(int r) {
 // lane 4 j + q points at row 4 (g / 2) + j and columns t*32 + 16 (g % 2) + 4 q
 // .. + 3; ds_read_b64_tr_b16 then leaves lane i with rows 4 (g / 2) .. + 3 of
 // column t*32 + 16 (g % 2) + i.  The second read of a 16-row k-step is 8 rows
-// further; those rows have another swizzle, hence two offsets per block.
-// Adding 16 rows leaves the swizzle unchanged.
+// further; those rows have another permutation, hence two offsets per block.
+// Adding 16 rows leaves the permutation unchanged.
 template <int D>
 __device__ inline void tr_offsets(int lane, int (&ofs)[D / 32][2]) {
   constexpr int CPR = D / 8;
@@ -104,23 +114,16 @@ __device__ inline void tr_offsets(int lane, int (&ofs)[D / 32][2]) {
     }
 }
 
-// The same offsets from two registers: block t is block t % 2 shifted by
-// 8 chunks (64 elements) for t >= 2 (d = 128), and the second read is 8 rows
-// further with the chunk bit 3 flipped (d = 128) or unchanged (d = 64).
 template <int D>
 struct TrOfs {
-  int b0, b1;   // offsets of blocks 0 and 1, first read
-  __device__ inline int at(int t, int half) const {
-    int o = ((t & 1) ? b1 : b0) + 64 * (t >> 1) + half * 8 * D;
-    if (D == 128 && half) o += (t < 2) ? 64 : -64;
-    return o;
-  }
+  int o[D / 32][2];   // block t, first / second read
+  __device__ inline int at(int t, int half) const { return o[t][half]; }
 };
 template <int D>
 __device__ inline TrOfs<D> tr_offsets2(int lane) {
-  int ofs[D / 32][2];
-  tr_offsets<D>(lane, ofs);
-  return TrOfs<D>{ofs[0][0], ofs[1][0]};
+  TrOfs<D> r;
+  tr_offsets<D>(lane, r.o);
+  return r;
 }
 
 // A operand of a 32x32x16 product whose k index runs over 16 rows of a tile
