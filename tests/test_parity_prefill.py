@@ -106,6 +106,9 @@ SHAPES = [
     (1, 384, 384, 8, 1, 128, "bf16", True),     # GQA 8:1
     (2, 300, 300, 3, 1, 128, "bf16", True),     # odd group: 256 rows of one head per workgroup
     (1, 600, 250, 6, 2, 128, "bf16", True),     # odd group, Nq > Nk: whole waves see no key
+    (1, 64, 64, 2, 2, 128, "bf16", True),       # one key tile: first tile is also the last
+    (1, 65, 65, 2, 1, 128, "bf16", False),      # a second tile with one key
+    (1, 129, 129, 4, 2, 64, "f16", True),       # pipeline ends one row / key past a tile
     (2, 96, 96, 3, 1, 128, "f32", True),
     (1, 200, 77, 2, 2, 64, "f32", False),
     (1, 513, 513, 2, 1, 128, "f32", True),
