@@ -115,6 +115,53 @@ SHAPES = [
 ]
 
 
+def _random_cases(n, seed):
+    """Seeded random prefill problems: sizes that straddle tile and block
+    edges, GQA ratios 1..8, both head dims and 16-bit dtypes, both masks,
+    and head-major (strided) layouts for some operands."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        grp = int(rng.choice([1, 2, 3, 4, 8]))
+        cases.append(dict(B=int(rng.integers(1, 3)), Nq=int(rng.integers(1, 400)),
+                          Nk=int(rng.integers(1, 400)), Hq=hkv * grp, Hkv=hkv,
+                          d=int(rng.choice([64, 128])), dt=str(rng.choice(["bf16", "f16"])),
+                          causal=bool(rng.integers(0, 2)), strided=int(rng.integers(0, 8)),
+                          seed=1000 + i))
+    return cases
+
+
+def _head_major(t):
+    """The same values laid out [B][H][N][d] and viewed as [B][N][H][d]."""
+    B, N, H, d = t.shape
+    out = torch.empty(B, H, N, d, dtype=t.dtype, device=t.device).transpose(1, 2)
+    out.copy_(t)
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 77), ids=lambda c: "seed%d" % c["seed"])
+def test_random_shapes(case):
+    c = case
+    inp = workloads.prefill_inputs(c["B"], c["Nq"], c["Nk"], c["Hq"], c["Hkv"], c["d"], c["dt"],
+                                   seed=c["seed"], causal=c["causal"])
+    what = "random %s" % (c,)
+    print("case:", what, flush=True)
+    q, k, v = (x.to(DEV) for x in (inp.q, inp.k, inp.v))
+    # bit i of `strided`: operand i (q, k, v) in head-major layout
+    if c["strided"] & 1:
+        q = _head_major(q)
+    if c["strided"] & 2:
+        k = _head_major(k)
+    if c["strided"] & 4:
+        v = _head_major(v)
+    o, lse = ea.attn_fwd(q, k, v, causal=inp.causal, scale=inp.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.sdpa(_np(inp.q), _np(inp.k), _np(inp.v), inp.scale, inp.causal)
+    assert_close(o, ref, TDT[inp.dtype], what)
+    assert_lse_close(lse, ref_lse, TDT[inp.dtype], what=what)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_shapes(shape):
     B, Nq, Nk, Hq, Hkv, d, dt, causal = shape
