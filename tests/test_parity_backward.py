@@ -136,6 +136,27 @@ def test_strided_views():
     _case(1, 190, 190, 2, 1, 128, "bf16", False, seed=95, strided=True)
 
 
+def _random_cases(n, seed):
+    """Seeded random backward problems: ragged sizes around the 64- and
+    128-row tiles, GQA ratios 1..4, both head dims and dtypes, both masks,
+    and wide-buffer (strided) views."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2]))
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 300)), int(rng.integers(1, 300)),
+                    hkv * int(rng.choice([1, 2, 3, 4])), hkv, int(rng.choice([64, 128])),
+                    str(rng.choice(["bf16", "f16"])), bool(rng.integers(0, 2)), 2000 + i,
+                    bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(12, 55), ids=lambda c: "seed%d" % c[8])
+def test_random_problems(case):
+    B, nq, nk, hq, hkv, d, dt, causal, seed, strided = case
+    _case(B, nq, nk, hq, hkv, d, dt, causal, seed=seed, strided=strided)
+
+
 def test_deterministic():
     q, k, v, o, g, lse, (dq, dk, dv) = _case(1, 300, 300, 4, 1, 128, "bf16", True, seed=96)
     dq2, dk2, dv2 = ea.attn_bwd(q, k, v, o, g, lse, causal=True)
