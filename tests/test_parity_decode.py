@@ -158,3 +158,28 @@ def test_long_contexts_large_groups(group, h_kv, lo, hi):
     # groups of 8 and 16 query heads at d = 128 run one wave per SIMD
     inp = _long_case(group * h_kv, h_kv, lo, hi, 61 + group)
     _check(inp, "long contexts, group %d" % group)
+
+
+def _random_cases(n, seed):
+    """Seeded random decode batches: 1..40 sequences with contexts from 0 to
+    3000 tokens (block edges included by chance), GQA ratios 1..16, both head
+    dims and dtypes; NaN in every slot past a context."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        s = int(rng.integers(1, 41))
+        ctx = [int(c) for c in rng.integers(0, 3001, s)]
+        h_kv = int(rng.choice([1, 2, 4, 8]))
+        group = int(rng.choice([1, 2, 4, 8, 16]))
+        out.append((ctx, h_kv * group, h_kv, int(rng.choice([64, 128])),
+                    str(rng.choice(["bf16", "f16"])), 3000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(12, 66), ids=lambda c: "seed%d" % c[5])
+def test_random_batches(case):
+    ctx, h_q, h_kv, d, dt, seed = case
+    inp = workloads.decode_inputs(ctx, h_q=h_q, h_kv=h_kv, d=d, block_size=16, dtype=dt,
+                                  seed=seed)
+    _check(inp, "random %d seqs ctx<=%d %d/%d heads d=%d %s" % (len(ctx), max(ctx), h_q, h_kv,
+                                                               d, dt))
