@@ -22,6 +22,8 @@ Prints one JSON line:
                  the same prefill read back through the block table with
                  attn_fwd_paged (TFLOP/s, beside the contiguous attn_fwd)
   cpu_baseline   the fp64 CPU oracle timed on the host on a bounded sample
+With --only long, the long causal GQA prefill (B=1, 32/8 heads, N=16384,
+d=128, bf16) alone, timed over back-to-back calls, as {"long_prefill": ...}.
 Kernel times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -86,7 +88,7 @@ def parse():
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-prefix decode measurement (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward", "paged"],
+    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward", "paged", "long"],
                     default=None,
                     help="run one kernel family only (for profiling)")
     ap.add_argument("--write-traffic", nargs="+", default=None, metavar="DIR")
@@ -307,6 +309,40 @@ def backward(ea, pre, q, k, v, pre_flops, reps):
     }
 
 
+def long_prefill(ea, workloads, dev, reps):
+    """The long causal GQA prefill (B=1, 32 query / 8 KV heads, N=16384,
+    d=128, bf16), timed over `reps` back-to-back calls with HIP events on the
+    current stream."""
+    inp = workloads.prefill_config(3)
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    o = torch.empty_like(q)
+    B, N, Hq, d = q.shape
+    flops = workloads.prefill_flops(B, N, N, Hq, d, True)
+
+    def run():
+        ea.attn_fwd(q, k, v, causal=True, scale=inp.scale, out=o)
+
+    for _ in range(2):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": "causal prefill B=1 Hq=32 Hkv=8 N=16384 d=128 bf16",
+        "mean_ms": ms, "value": tf, "unit": "TFLOP/s", "flop_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "kernel": "attn_fwd_mfma_kernel<bf16,128,causal>"},
+        "note": "back-to-back calls",
+    }
+
+
 def paged_kv(ea, pre, q, k, v, pre_flops, reps):
     """paged_kv_write of the prefill workload's K and V into a shuffled paged
     cache, then attn_fwd_paged over it; each timed over `reps` back-to-back
@@ -380,6 +416,10 @@ def main():
     pre_flops = workloads.prefill_flops(B, N, N, Hq, d, True)
     q, k, v = (x.to(dev) for x in (pre.q, pre.k, pre.v))
     o = torch.empty_like(q)
+    if args.only == "long":
+        print(json.dumps({"long_prefill": long_prefill(ea, workloads, dev, args.steps)}),
+              flush=True)
+        return
     if args.only == "shared":
         print(json.dumps({"shared_decode": shared_decode(ea, workloads, dev, args.steps)}),
               flush=True)
