@@ -22,7 +22,7 @@ __all__ = [
     "paged_attn_decode",
     "paged_attn_decode_workspace_size", "paged_attn_decode_shared",
     "paged_attn_decode_shared_workspace_size", "paged_kv_write", "paged_kv_copy_blocks",
-    "attn_fwd_paged",
+    "attn_fwd_paged", "validate_paged_tables",
     "BlockManager", "LIB_PATH",
 ]
 
@@ -93,6 +93,8 @@ def lib():
     L.paged_kv_write.argtypes = [i32, vp, vp, i64p, i64p, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.paged_kv_copy_blocks.restype = i32
     L.paged_kv_copy_blocks.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.attn_validate_paged_tables.restype = i32
+    L.attn_validate_paged_tables.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, i32]
     L.attn_bm_create.restype = i32
     L.attn_bm_create.argtypes = [i32, i32, ctypes.POINTER(vp)]
     L.attn_bm_destroy.restype = None
@@ -494,3 +496,32 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, context_lens, max_context_l
     if return_lse:
         return out, lse
     return out
+
+
+def validate_paged_tables(block_table, context_lens, max_context_len, num_blocks, block_size=16,
+                          group_starts=None, prefix_lens=None):
+    """Host range check of a paged call's metadata (the C ABI's
+    attn_validate_paged_tables): ``block_table`` ``[S][max_blocks]`` and
+    ``context_lens`` ``[S]``, optionally ``group_starts`` ``[G + 1]`` and
+    ``prefix_lens`` ``[G]``, as int32 host arrays (numpy or CPU tensors).
+    Raises :class:`AttnError` naming the first violation."""
+    import numpy as np
+
+    def host(x):
+        if x is None:
+            return None
+        if torch.is_tensor(x):
+            x = x.cpu().numpy()
+        return np.ascontiguousarray(x, dtype=np.int32)
+
+    tab, ctx = host(block_table), host(context_lens)
+    gs, pl = host(group_starts), host(prefix_lens)
+    if tab.ndim != 2 or ctx.shape != (tab.shape[0],):
+        raise ValueError("block_table must be [S][max_blocks] and context_lens [S]")
+    G = 0 if pl is None else pl.shape[0]
+    if gs is not None and gs.shape != (G + 1,):
+        raise ValueError("group_starts must have one more entry than prefix_lens")
+    p = lambda a: None if a is None else ctypes.c_void_p(a.ctypes.data)
+    _check(lib().attn_validate_paged_tables(p(tab), p(ctx), tab.shape[0], tab.shape[1],
+                                            int(max_context_len), int(num_blocks),
+                                            int(block_size), p(gs), p(pl), G))

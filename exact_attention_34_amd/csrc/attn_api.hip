@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "common.h"
@@ -149,6 +150,50 @@ int check_workspace(const char* fn, void* workspace, size_t workspace_bytes, siz
   if (!aligned16(workspace))
     return fail(ATTN_ERR_ALIGN, std::string(fn) + ": workspace must be 16-byte aligned");
   return ATTN_OK;
+}
+
+// ATTN_VALIDATE set to anything but "" or "0": the paged entry points copy
+// their device metadata to the host and range-check it before any launch.
+// Read at every call, so a test can switch it.
+bool validate_enabled() {
+  const char* e = std::getenv("ATTN_VALIDATE");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+// n int32 values from device memory to `out`, ordered after the work already
+// on `stream` (the caller may have written them there).
+int fetch_i32(const char* fn, const int32_t* dev, size_t n, std::vector<int32_t>& out,
+              hipStream_t stream) {
+  out.assign(n, 0);
+  if (n == 0 || dev == nullptr) return ATTN_OK;
+  hipError_t e = hipMemcpyAsync(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(ATTN_ERR_HIP, std::string(fn) + ": copy for ATTN_VALIDATE failed: " +
+                                  hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+// The ATTN_VALIDATE check: host copies of the table, the context lengths
+// and (shared-prefix decode) the groups, through attn_validate_paged_tables.
+int validate_on_host(const char* fn, hipStream_t stream, const int32_t* block_table,
+                     const int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
+                     int max_context_len, int num_blocks, int block_size,
+                     const int32_t* group_starts, const int32_t* prefix_lens, int num_groups) {
+  std::vector<int32_t> tab, ctx, gs, pl;
+  int rc = fetch_i32(fn, block_table, (size_t)num_seqs * max_blocks_per_seq, tab, stream);
+  if (rc == ATTN_OK) rc = fetch_i32(fn, context_lens, (size_t)num_seqs, ctx, stream);
+  if (rc == ATTN_OK && group_starts != nullptr)
+    rc = fetch_i32(fn, group_starts, (size_t)num_groups + 1, gs, stream);
+  if (rc == ATTN_OK && prefix_lens != nullptr)
+    rc = fetch_i32(fn, prefix_lens, (size_t)num_groups, pl, stream);
+  if (rc != ATTN_OK) return rc;
+  rc = attn_validate_paged_tables(tab.data(), ctx.data(), num_seqs, max_blocks_per_seq,
+                                  max_context_len, num_blocks, block_size,
+                                  group_starts != nullptr ? gs.data() : nullptr,
+                                  prefix_lens != nullptr ? pl.data() : nullptr, num_groups);
+  if (rc != ATTN_OK) g_last_error = std::string(fn) + " (ATTN_VALIDATE): " + g_last_error;
+  return rc;
 }
 
 bool debug_enabled() {
@@ -301,6 +346,13 @@ int attn_fwd_paged(int dtype, const void* q, const int64_t* q_stride, const void
       return fail(ATTN_ERR_UNSUPPORTED, f + ": one (batch, head) slice of q spans >= 2 GiB");
     if ((int64_t)((n_q + 63) / 64) * batch * h_q > (int64_t)1 << 31)
       return fail(ATTN_ERR_UNSUPPORTED, f + ": problem too large for one launch");
+    if (validate_enabled()) {
+      const int rc = validate_on_host("attn_fwd_paged", reinterpret_cast<hipStream_t>(stream),
+                                      block_table, context_lens, batch, max_blocks_per_seq,
+                                      max_context_len, num_blocks, block_size, nullptr, nullptr,
+                                      0);
+      if (rc != ATTN_OK) return rc;
+    }
     attn::FwdParams p{};
     p.q = q;
     p.k = k_cache;
@@ -501,21 +553,25 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int h_kv, int hea
   return attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
 }
 
-int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_table, const int32_t* context_lens, void* o,
-                      float* lse, int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
-                      int max_blocks_per_seq, int max_context_len, int num_blocks,
-                      float softmax_scale, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_attn_decode.
+int decode_call(const char* fn, int dtype, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                void* o, float* lse, int num_seqs, int h_q, int h_kv, int head_dim,
+                int block_size, int max_blocks_per_seq, int max_context_len, int num_blocks,
+                float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     g_last_error.clear();
     attn::DecodeParams p;
-    int rc = check_decode("paged_attn_decode", dtype, q, k_cache, v_cache, block_table,
-                          context_lens, o, lse, num_seqs, h_q, h_kv, head_dim, block_size,
-                          max_blocks_per_seq, max_context_len, num_blocks, softmax_scale, p);
+    int rc = check_decode(fn, dtype, q, k_cache, v_cache, block_table, context_lens, o, lse,
+                          num_seqs, h_q, h_kv, head_dim, block_size, max_blocks_per_seq,
+                          max_context_len, num_blocks, softmax_scale, p);
     if (rc != ATTN_OK || num_seqs == 0) return rc;
     const size_t need = attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
-    rc = check_workspace("paged_attn_decode", workspace, workspace_bytes, need);
+    rc = check_workspace(fn, workspace, workspace_bytes, need);
     if (rc != ATTN_OK) return rc;
     if (need > 0) {
       const int64_t slots =
@@ -524,17 +580,39 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
       p.ws_ml = p.ws_o + slots * head_dim;
       p.ws_unit = reinterpret_cast<int32_t*>(p.ws_ml + slots * 2);
     }
+    if (validate_enabled()) {
+      rc = validate_on_host(fn, reinterpret_cast<hipStream_t>(stream),
+                            block_table, context_lens, num_seqs, max_blocks_per_seq,
+                            max_context_len, num_blocks, block_size, nullptr, nullptr, 0);
+      if (rc != ATTN_OK) return rc;
+    }
     if (debug_enabled())
-      std::fprintf(stderr, "[attn] paged_attn_decode dtype=%d seqs=%d hq=%d hkv=%d d=%d waves=%d\n",
+      std::fprintf(stderr, "[attn] %s dtype=%d seqs=%d hq=%d hkv=%d d=%d waves=%d\n", fn,
                    dtype, num_seqs, h_q, h_kv, head_dim,
                    attn::decode_waves(num_seqs, h_kv, max_context_len));
     hipError_t e = attn::launch_decode(dtype, p, max_context_len, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
-      return fail(ATTN_ERR_HIP, std::string("paged_attn_decode: launch failed: ") + hipGetErrorString(e));
+      return fail(ATTN_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
     return ATTN_OK;
   } catch (...) {
-    return fail(ATTN_ERR_HIP, "paged_attn_decode: unexpected host exception");
+    return fail(ATTN_ERR_HIP, std::string(fn) + ": unexpected host exception");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* context_lens, void* o,
+                      float* lse, int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                      int max_blocks_per_seq, int max_context_len, int num_blocks,
+                      float softmax_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_call("paged_attn_decode", dtype, q, k_cache, v_cache, block_table, context_lens,
+                     o, lse, num_seqs, h_q, h_kv, head_dim, block_size, max_blocks_per_seq,
+                     max_context_len, num_blocks, softmax_scale, workspace, workspace_bytes,
+                     stream);
 }
 
 size_t paged_attn_decode_shared_workspace_size(int num_seqs, int num_groups, int max_group_size,
@@ -584,6 +662,12 @@ int paged_attn_decode_shared(int dtype, const void* q, const void* k_cache, cons
     const SharedWs lay = shared_ws(num_seqs, h_q, head_dim, split, pl.items);
     rc = check_workspace(fn, workspace, workspace_bytes, lay.total);
     if (rc != ATTN_OK) return rc;
+    if (validate_enabled()) {
+      rc = validate_on_host(fn, reinterpret_cast<hipStream_t>(stream), block_table, context_lens,
+                            num_seqs, max_blocks_per_seq, max_context_len, num_blocks,
+                            block_size, group_starts, prefix_lens, num_groups);
+      if (rc != ATTN_OK) return rc;
+    }
     char* base = static_cast<char*>(workspace);
     if (split > 0) {
       const int64_t slots =

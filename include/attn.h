@@ -37,7 +37,13 @@
  * passed as void*; NULL means the null stream) and never synchronise.  A
  * device-side fault caused by invalid device data (an out-of-range block id,
  * a context length above the stated maximum) surfaces at the caller's next
- * synchronisation and is undefined behaviour.
+ * synchronisation and is undefined behaviour.  Test mode: with the
+ * environment variable ATTN_VALIDATE set to a value other than "0", the
+ * paged entry points (paged_attn_decode, paged_attn_decode_shared,
+ * attn_fwd_paged) first copy their block table, context lengths and groups
+ * to the host, waiting for the copy on the given stream, and check them with
+ * attn_validate_paged_tables; a violation returns ATTN_ERR_SHAPE and launches
+ * nothing.  The variable is read at every call.
  *
  * Errors.  Every entry point returns ATTN_OK or one of the codes below and
  * never aborts; no C++ exception crosses the ABI.  Arguments are validated on
@@ -54,7 +60,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 /* element types of q, k, v, o and the KV cache */
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -77,6 +83,37 @@ int attn_abi_version(void);
 /* Message for the last non-OK status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 const char* attn_last_error(void);
+
+/*
+ * attn_validate_paged_tables -- range-check the metadata of a paged call on
+ * the host (every array is HOST memory; nothing touches the GPU).  The
+ * kernels trust these values; this is the check the ATTN_VALIDATE mode runs.
+ * The contract checked is the paged KV cache of the tutorial "Chapter 3
+ * Advanced principles: performance model and numerical stability", section
+ * 3.0: logical block t / block_size of a sequence lives in the physical block
+ * its table row names, and sequences sharing a prefix name the same blocks.
+ *
+ *   block_table     [num_seqs][max_blocks_per_seq] int32; the first
+ *                   ceil(context_lens[s] / block_size) entries of row s must
+ *                   lie in [0, num_blocks) (the rest are not read).
+ *   context_lens    [num_seqs] int32, each in [0, max_context_len] and
+ *                   needing at most max_blocks_per_seq table entries.
+ *   group_starts,   NULL (no groups) or, for paged_attn_decode_shared,
+ *   prefix_lens     [num_groups + 1] and [num_groups] int32 with
+ *                   group_starts[0] == 0, non-decreasing, group_starts[
+ *                   num_groups] == num_seqs; prefix_lens[g] >= 0 and at most
+ *                   every member's context; the first prefix_lens[g] /
+ *                   block_size entries of every member's row equal the
+ *                   group's first member's.
+ *
+ * Returns ATTN_OK, ATTN_ERR_NULL (a required array is NULL) or
+ * ATTN_ERR_SHAPE; attn_last_error() names the first violation found (array,
+ * index, value).
+ */
+int attn_validate_paged_tables(const int32_t* block_table, const int32_t* context_lens,
+                               int num_seqs, int max_blocks_per_seq, int max_context_len,
+                               int num_blocks, int block_size, const int32_t* group_starts,
+                               const int32_t* prefix_lens, int num_groups);
 
 /*
  * attn_fwd -- prefill: O = softmax(Q K^T * softmax_scale [+ causal mask]) V.
@@ -259,9 +296,12 @@ size_t paged_attn_decode_shared_workspace_size(int num_seqs, int num_groups, int
  *                       whole blocks are read once per group; a partial last
  *                       block is read per sequence like the rest.
  *   num_groups          >= 1 (when num_seqs > 0).
- *   max_group_size      host-side upper bound of the group sizes.
- *   max_prefix_len      host-side upper bound of prefix_lens, at most
- *                       max_context_len.
+ *   max_group_size      host-side bound of the group sizes and
+ *   max_prefix_len      of prefix_lens (at most max_context_len), which size
+ *                       the prefix work and the workspace.  Members and
+ *                       prefix blocks past these bounds are left to the
+ *                       per-sequence pass: a bound below the actual value
+ *                       costs speed, not correctness.
  *   workspace           at least paged_attn_decode_shared_workspace_size(
  *                       num_seqs, num_groups, max_group_size, h_q, h_kv,
  *                       head_dim, max_context_len, max_prefix_len) bytes,

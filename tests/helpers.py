@@ -15,6 +15,8 @@ No NaN or Inf is allowed anywhere.
 import numpy as np
 import torch
 
+import oracle
+
 MANT_BITS = {torch.bfloat16: 7, torch.float16: 10, torch.float32: 23}
 
 
@@ -84,3 +86,22 @@ def assert_lse_close(gpu_lse, ref_lse, dtype, what=""):
         print("%s lse max-abs %.3e (worst err/bound %.2f)" % (what, err.max(), (err / bound).max()),
               flush=True)
         assert np.all(err <= bound), "%s: lse error %.3e" % (what, err.max())
+
+
+def decode_reference(inp):
+    """The oracle's single-token decode result, computed from each sequence's
+    logical, contiguous K/V (``inp.k_logical``, ``inp.v_logical``): the query
+    row of sequence s attends to all of its context by the definition, with
+    no block table involved, so a layout mistake shared by the cache builder
+    and the kernel cannot pass.  Returns (o [S][Hq][d], lse [S][Hq])."""
+    S, Hq, d = inp.q.shape
+    assert len(inp.k_logical) == S and len(inp.v_logical) == S
+    o = np.zeros((S, Hq, d))
+    lse = np.full((S, Hq), -np.inf)
+    for s in range(S):
+        k = inp.k_logical[s].double().numpy()[None]
+        v = inp.v_logical[s].double().numpy()[None]
+        oo, ll = oracle.sdpa(inp.q[s].double().numpy()[None, None], k, v, inp.scale, False)
+        o[s] = oo[0, 0]
+        lse[s] = ll[0, :, 0]
+    return o, lse

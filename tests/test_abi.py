@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ea.abi_version() == 6
+    assert ea.abi_version() == 7
 
 
 def test_workspace_size():
@@ -238,3 +238,70 @@ def test_last_error_cleared_on_success():
     assert ea.lib().attn_last_error().decode() != ""
     assert _fwd(batch=0)[0] == 0
     assert ea.lib().attn_last_error().decode() == ""
+
+
+# ----------------------------------------------------------------------------
+# attn_validate_paged_tables: the check behind the ATTN_VALIDATE mode, on host
+# arrays (no GPU involved)
+# ----------------------------------------------------------------------------
+
+def _tables():
+    import numpy as np
+    # 3 sequences of 40, 16 and 0 tokens in 16-token blocks; the first two
+    # form a group sharing a 16-token prefix (block 7), the third its own group
+    tab = np.full((3, 4), -1, dtype=np.int32)
+    tab[0, :3] = [7, 2, 5]
+    tab[1, :1] = [7]
+    ctx = np.array([40, 16, 0], dtype=np.int32)
+    gs = np.array([0, 2, 3], dtype=np.int32)
+    pl = np.array([16, 0], dtype=np.int32)
+    return tab, ctx, gs, pl
+
+
+def test_validate_accepts_valid_tables():
+    tab, ctx, gs, pl = _tables()
+    ea.validate_paged_tables(tab, ctx, max_context_len=64, num_blocks=8)
+    ea.validate_paged_tables(tab, ctx, 64, 8, group_starts=gs, prefix_lens=pl)
+    # an empty batch, and entries past a context are never read (-1 there)
+    ea.validate_paged_tables(tab[:0], ctx[:0], 64, 8)
+
+
+def _rejects(match, **kw):
+    tab, ctx, gs, pl = _tables()
+    args = dict(block_table=tab, context_lens=ctx, max_context_len=64, num_blocks=8,
+                group_starts=gs, prefix_lens=pl)
+    mutate = kw.pop("mutate")
+    mutate(args)
+    args.update(kw)
+    with pytest.raises(ea.AttnError) as ei:
+        ea.validate_paged_tables(**args)
+    assert ei.value.code == 2 and re.search(match, str(ei.value)), str(ei.value)
+
+
+def test_validate_rejects_block_id_out_of_range():
+    _rejects(r"block_table\[0\]\[2\] = 8 outside", mutate=lambda a: a["block_table"].__setitem__((0, 2), 8))
+    _rejects(r"block_table\[0\]\[1\] = -1 outside", mutate=lambda a: a["block_table"].__setitem__((0, 1), -1))
+
+
+def test_validate_rejects_context_lengths():
+    _rejects(r"context_lens\[2\] = -3", mutate=lambda a: a["context_lens"].__setitem__(2, -3))
+    _rejects(r"context_lens\[0\] = 40 outside", mutate=lambda a: None, max_context_len=39)
+    # 65 tokens need 5 entries of a 4-entry row
+    _rejects(r"needs 5 table entries", mutate=lambda a: a["context_lens"].__setitem__(0, 65),
+             max_context_len=100)
+
+
+def test_validate_rejects_bad_groups():
+    _rejects(r"group_starts\[0\] must be 0", mutate=lambda a: a["group_starts"].__setitem__(0, 1))
+    _rejects(r"must equal num_seqs", mutate=lambda a: a["group_starts"].__setitem__(2, 2))
+    _rejects(r"non-decreasing", mutate=lambda a: a["group_starts"].__setitem__(1, 4))
+    _rejects(r"prefix_lens\[1\] = -1", mutate=lambda a: a["prefix_lens"].__setitem__(1, -1))
+    # a 17-token prefix is longer than member 1's 16-token context
+    _rejects(r"exceeds context_lens\[1\]", mutate=lambda a: a["prefix_lens"].__setitem__(0, 17))
+
+
+def test_validate_rejects_prefix_blocks_that_are_not_shared():
+    def mutate(a):
+        a["block_table"][1, 0] = 3
+    _rejects(r"block_table\[1\]\[0\] = 3 differs", mutate=mutate)
+

@@ -7,9 +7,8 @@ import pytest
 import torch
 
 import exact_attention_34_amd as ea
-import oracle
 import workloads
-from helpers import assert_close, assert_lse_close
+from helpers import assert_close, assert_lse_close, decode_reference
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -26,9 +25,7 @@ def _run(inp, **kw):
 
 
 def _oracle(inp):
-    return oracle.paged_decode(inp.q.double().numpy(), inp.k_cache.float().numpy(),
-                               inp.v_cache.float().numpy(), inp.block_table.numpy(),
-                               inp.context_lens.numpy(), inp.block_size, inp.scale)
+    return decode_reference(inp)
 
 
 def _check(inp, what):
@@ -183,3 +180,12 @@ def test_random_batches(case):
                                   seed=seed)
     _check(inp, "random %d seqs ctx<=%d %d/%d heads d=%d %s" % (len(ctx), max(ctx), h_q, h_kv,
                                                                d, dt))
+
+
+def test_validate_mode_on_valid_inputs(config4, monkeypatch):
+    # ATTN_VALIDATE=1: the call range-checks host copies of the table and the
+    # context lengths first; valid inputs then give the same bits
+    out1, lse1 = _run(config4)
+    monkeypatch.setenv("ATTN_VALIDATE", "1")
+    out2, lse2 = _run(config4)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)

@@ -10,9 +10,8 @@ import pytest
 import torch
 
 import exact_attention_34_amd as ea
-import oracle
 import workloads
-from helpers import assert_close, assert_lse_close
+from helpers import assert_close, assert_lse_close, decode_reference
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -47,9 +46,7 @@ def _run_plain(inp):
 
 
 def _oracle(inp):
-    return oracle.paged_decode(inp.q.double().numpy(), inp.k_cache.float().numpy(),
-                               inp.v_cache.float().numpy(), inp.block_table.numpy(),
-                               inp.context_lens.numpy(), inp.block_size, inp.scale)
+    return decode_reference(inp)
 
 
 def _check(inp, what, **kw):
@@ -172,3 +169,12 @@ def test_prefix_in_extreme_logit_range():
     stressed = workloads.DecodeInputs(inp.q, kc, vc, tab, ctx, 16, inp.scale, "bf16", kl,
                                       inp.v_logical, inp.group_starts, inp.prefix_lens)
     _check(stressed, "x20 prefix keys")
+
+
+def test_validate_mode_on_valid_inputs(config5, monkeypatch):
+    # ATTN_VALIDATE=1 also checks the groups and that members share the
+    # prefix's block ids; valid inputs give the same bits
+    out1, lse1 = _run_shared(config5)
+    monkeypatch.setenv("ATTN_VALIDATE", "1")
+    out2, lse2 = _run_shared(config5)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)

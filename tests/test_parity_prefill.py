@@ -1,9 +1,11 @@
 """GPU parity of attn_fwd (prefill) against the fp64 oracle, through the C ABI.
 
 Full-size cases use the standard workloads in the launch configuration the
-benchmark times; the long causal GQA workload (N = 16384) is compared on
-sampled rows, each computed by the oracle against its head's whole K/V, plus
-properties that hold at any size.
+benchmark times.  The long causal GQA workload (N = 16384, 32 query / 8 KV
+heads) is compared element by element on all of its 524,288 output rows (the
+oracle takes about a minute of host CPU for it); a fast subset of sampled
+rows at tile edges runs first, and properties that hold at any size are
+checked on the whole output.
 """
 
 import math
@@ -86,6 +88,19 @@ def test_config3_long_causal_gqa_sampled():
     for h in range(Hq):
         assert (of[:, :, h, :] >= vmin[:, None, h // g, :] - 1e-2).all()
         assert (of[:, :, h, :] <= vmax[:, None, h // g, :] + 1e-2).all()
+
+
+@pytest.mark.timeout(1200)
+def test_config3_long_causal_gqa_full():
+    # every output row and log-sum-exp of the N = 16384 workload against the
+    # oracle (the launch the benchmark times: 1,024 work items of 256 rows,
+    # two query heads of a GQA group each, chunks of 2 items per XCD)
+    inp = workloads.prefill_config(3)
+    print("case: N=16384 Hq=32 Hkv=8 causal, all rows", flush=True)
+    o, lse = _run(inp)
+    ref, ref_lse = oracle.sdpa(_np(inp.q), _np(inp.k), _np(inp.v), inp.scale, True)
+    assert_close(o, ref, torch.bfloat16, "N=16384 all %d rows" % (ref.shape[1] * ref.shape[2]))
+    assert_lse_close(lse, ref_lse, torch.bfloat16, what="N=16384 all rows lse")
 
 
 # ----------------------------------------------------------------------------

@@ -68,3 +68,18 @@ def test_equals_contiguous_prefill_bitwise():
                          return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+def test_block_table_rows_longer_than_the_staged_part():
+    # contexts above 32,768 tokens: a workgroup stages the first 2,048 entries
+    # of its sequence's table row in LDS and reads the rest from memory
+    _case([40000, 33000, 2100], 200, 8, 2, 128, "bf16", True, seed=305)
+
+
+def test_block_table_rows_longer_than_the_staged_part_noncausal_fp16():
+    _case([36001], 130, 4, 4, 64, "f16", False, seed=306)
+
+
+def test_validate_mode_on_valid_inputs(monkeypatch):
+    monkeypatch.setenv("ATTN_VALIDATE", "1")
+    _case([300, 129], 128, 8, 2, 128, "bf16", True, seed=307)
