@@ -1,19 +1,29 @@
 """Benchmark of the hot path on one MI355X.
 
 One step = one causal prefill over the stress workload (batch 4, 16 heads,
-N = 2048, d = 128, bf16, 1 % of Q/K rows x20) followed by one paged decode over
-64 sequences (context lengths uniform in [512, 8192], 32 query / 8 KV heads,
-d = 128, bf16 KV cache in 16-token blocks, shuffled block table).  Inputs are
-synthetic (seeded) and resident in device memory before timing starts.
+N = 2048, d = 128, bf16, 1 % of Q/K rows x20), one long causal GQA prefill
+(batch 1, 32 query / 8 KV heads, N = 16384, d = 128, bf16) and one paged
+decode over 64 sequences (context lengths uniform in [512, 8192], 32 query /
+8 KV heads, d = 128, bf16 KV cache in 16-token blocks, shuffled block table).
+Inputs are synthetic (seeded) and resident in device memory before timing
+starts.
 
 Prints one JSON line:
-  value          prefill TFLOP/s (algorithmic FLOP / mean prefill kernel time)
-  roofline       prefill kernel against the dense bf16 matrix-core peak
+  value          prefill TFLOP/s of the stress workload (algorithmic FLOP /
+                 mean kernel time)
+  roofline       that prefill kernel against the dense bf16 matrix-core peak
+  long_prefill   the N = 16384 GQA prefill of the same step: TFLOP/s, its
+                 roofline, and the oracle timed on sampled rows of it
   decode         decode GB/s (algorithmic K/V bytes / mean decode time, split +
                  combine kernels) and its roofline against HBM bandwidth
+  achievable     what loops of the prefill's matrix op, of the exponential and
+                 of random 4 KiB reads reach on this chip (libattn_probes.so);
+                 each roofline also carries its fraction of these
   shared_decode  outside the step: the shared-prefix decode workload (8 groups
                  x 8 sequences, 4096-token common prefix, 256-token private
-                 suffixes), per-sequence decode against sharing-aware decode
+                 suffixes), per-sequence decode against sharing-aware decode,
+                 warm (one pool, back-to-back calls) and cold (three pools
+                 used in turn, 604 MB against the 256 MB last-level cache)
   backward       outside the step: attn_bwd on the prefill workload (its own
                  O and log-sum-exp, a seeded dO), TFLOP/s counted as 2.5x the
                  forward's algorithmic FLOP, against the bf16 peak
@@ -22,8 +32,9 @@ Prints one JSON line:
                  the same prefill read back through the block table with
                  attn_fwd_paged (TFLOP/s, beside the contiguous attn_fwd)
   cpu_baseline   the fp64 CPU oracle timed on the host on a bounded sample
-With --only long, the long causal GQA prefill (B=1, 32/8 heads, N=16384,
-d=128, bf16) alone, timed over back-to-back calls, as {"long_prefill": ...}.
+With --only long, the long causal GQA prefill alone, timed over back-to-back
+calls, as {"long_prefill": ...}; --only probes runs the achievable-peak
+probes alone.
 Kernel times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -59,8 +70,11 @@ CSRC = os.path.join(ROOT, "exact_attention_34_amd", "csrc")
 
 
 def source_hash():
+    """Hash of the attention library's sources (the probes are not part of it)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
+        if name == "probes.hip":
+            continue
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -87,38 +101,55 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-prefix decode measurement (for profiling)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="leave the N=16384 prefill out of the step (for profiling)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the achievable-peak probes")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward", "paged", "long"],
+    ap.add_argument("--only", choices=["prefill", "decode", "shared", "backward", "paged", "long",
+                                       "probes"],
                     default=None,
                     help="run one kernel family only (for profiling)")
     ap.add_argument("--write-traffic", nargs="+", default=None, metavar="DIR")
     return ap.parse_args()
 
 
-TRAFFIC_KERNELS = {   # entry name -> (kernel name prefix in rocprofv3 output, run)
-    "attn_fwd_mfma_kernel": ("void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true, false, 8>",
-                             "main"),
+_FWD = "void attn::attn_fwd_mfma_kernel<attn::BF16, 128, true, false, 8>"
+# entry name -> (kernel name prefix in rocprofv3 output, run, grid size in
+# work-items or None).  The two prefills of the step are one kernel; their
+# grids tell them apart: 512 workgroups of 512 threads (B=4, H=16, N=2048)
+# and 2,048 of them (N=16384, 32 query heads).
+TRAFFIC_KERNELS = {
+    "attn_fwd_mfma_kernel": (_FWD, "main", 512 * 512),
+    "attn_fwd_mfma_kernel_long": (_FWD, "main", 2048 * 512),
     "paged_decode_split_kernel": ("void attn::paged_decode_split_kernel<attn::BF16, 128, 4,",
-                                  "main"),
-    "paged_decode_combine_kernel": ("void attn::paged_decode_combine_kernel<attn::BF16", "main"),
+                                  "main", None),
+    "paged_decode_combine_kernel": ("void attn::paged_decode_combine_kernel<attn::BF16", "main",
+                                    None),
     "paged_decode_prefix_kernel": ("void attn::paged_decode_prefix_kernel<attn::BF16, 128>",
-                                   "shared"),
-    "attn_bwd_dkdv_kernel": ("void attn::attn_bwd_dkdv_kernel<attn::BF16, 128, true>", "backward"),
-    "attn_bwd_dq_kernel": ("void attn::attn_bwd_dq_kernel<attn::BF16, 128, true>", "backward"),
+                                   "shared", None),
+    "attn_bwd_dkdv_kernel": ("void attn::attn_bwd_dkdv_kernel<attn::BF16, 128, true>", "backward",
+                             None),
+    "attn_bwd_dq_kernel": ("void attn::attn_bwd_dq_kernel<attn::BF16, 128, true>", "backward",
+                           None),
 }
 
 
-def _counter_kib(directory, counter, prefix):
+def _counter_kib(directory, counter, prefix, grid=None):
     """Mean KiB per dispatch of `counter` over the kernels whose name starts
-    with `prefix`, from rocprofv3 counter_collection.csv files."""
+    with `prefix` (and, if given, whose grid has `grid` work-items), from
+    rocprofv3 counter_collection.csv files."""
     import csv
     import glob
     vals = []
     for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(prefix):
-                    vals.append(float(r["Counter_Value"]))
+                if r["Counter_Name"] != counter or not r["Kernel_Name"].startswith(prefix):
+                    continue
+                if grid is not None and int(float(r["Grid_Size"])) != grid:
+                    continue
+                vals.append(float(r["Counter_Value"]))
     if not vals:
         raise SystemExit("no %s samples for %s in %s" % (counter, prefix, directory))
     return float(np.mean(vals)), len(vals)
@@ -142,15 +173,15 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, sfetch_d
                   "source_hash." % (ff, wf),
         "fetch_factor": ff, "write_factor": wf,
     }
-    for name, (prefix, run) in TRAFFIC_KERNELS.items():
+    for name, (prefix, run, grid) in TRAFFIC_KERNELS.items():
         fd, wd = {"main": (fetch_dir, write_dir), "shared": (sfetch_dir, swrite_dir),
                   "backward": (bfetch_dir, bwrite_dir)}[run]
         if fd is None:
             continue
-        fk, n1 = _counter_kib(fd, "FETCH_SIZE", prefix)
-        wk, n2 = _counter_kib(wd, "WRITE_SIZE", prefix)
+        fk, n1 = _counter_kib(fd, "FETCH_SIZE", prefix, grid)
+        wk, n2 = _counter_kib(wd, "WRITE_SIZE", prefix, grid)
         fb, wb = int(round(fk * 1024 * ff)), int(round(wk * 1024 * wf))
-        out[name] = {"kernel_prefix": prefix, "source_hash": source_hash(),
+        out[name] = {"kernel_prefix": prefix, "grid_size": grid, "source_hash": source_hash(),
                      "fetch_kib_raw": fk, "write_kib_raw": wk, "dispatches": [n1, n2],
                      "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
     with open(TRAFFIC_FILE, "w") as f:
@@ -170,14 +201,23 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
 
 
+def blas_info():
+    """(threads, vendor) of the BLAS numpy uses, as threadpoolctl reports them."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p.get("num_threads", 1) for p in info] + [1])
+        vendor = ", ".join("%s %s (%s)" % (p.get("internal_api"), p.get("version"),
+                                            p.get("threading_layer", "?")) for p in info)
+        return threads, vendor or "unknown"
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0)), "unknown"
+
+
 def cpu_baseline(pre, dec, dec_bytes, pre_flops):
     """Time the fp64 oracle on a bounded sample of the same workloads."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads, vendor = blas_info()
     q, k, v = (x.float().numpy() for x in (pre.q, pre.k, pre.v))
     # prefill sample: the whole stress workload (64 (batch, head) pairs)
     t0 = time.perf_counter()
@@ -194,48 +234,62 @@ def cpu_baseline(pre, dec, dec_bytes, pre_flops):
     bytes_sample = int(dec.context_lens[:ns].to(torch.int64).sum()) * 8 * 128 * 2 * 2
     return {
         "value": flops_sample / t_pre / 1e12, "unit": "TFLOP/s", "cores": threads,
-        "kind": "oracle",
+        "kind": "oracle", "blas": vendor,
         "sample": "one pass of each workload: prefill B=4 H=16 N=2048 causal (%.1f s), "
                   "decode of all 64 sequences (%.1f s)" % (t_pre, t_dec),
         "decode_value": bytes_sample / t_dec / 1e9, "decode_unit": "GB/s",
     }
 
 
-def shared_decode(ea, workloads, dev, reps):
-    """Per-sequence decode against sharing-aware decode on the shared-prefix
-    workload, each timed over `reps` back-to-back calls with HIP events on
-    the current stream.  GB/s are reported on the logical bytes (what a
-    per-sequence kernel reads) and on the unique bytes (each shared block
-    once)."""
-    inp = workloads.decode_config5(nan_fill=True)
-    q, kc, vc = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev)
-    tab, ctx = inp.block_table.to(dev), inp.context_lens.to(dev)
-    gs, pl = inp.group_starts.to(dev), inp.prefix_lens.to(dev)
-    S, Hq, d = q.shape
-    Hkv = kc.shape[1]
-    G = pl.shape[0]
-    mcl = inp.max_context_len
-    mgs = int(np.diff(inp.group_starts.numpy()).max())
-    mpl = int(inp.prefix_lens.max())
-    out = torch.empty_like(q)
-    ws_plain = torch.empty(ea.paged_attn_decode_workspace_size(S, Hq, Hkv, d, mcl),
-                           dtype=torch.uint8, device=dev)
-    ws_shared = torch.empty(ea.paged_attn_decode_shared_workspace_size(S, G, mgs, Hq, Hkv, d,
-                                                                       mcl, mpl),
-                            dtype=torch.uint8, device=dev)
+def long_prefill_cpu_baseline(inp, n_rows=512, seed=33):
+    """The oracle on sampled rows of the N = 16384 GQA prefill: n_rows
+    (batch, row, head) triples, each attending to its whole visible key range
+    (row i of a causal sequence sees i + 1 keys: 4 d (i + 1) FLOP)."""
+    import oracle
+    threads, vendor = blas_info()
+    B, N, Hq, d = inp.q.shape
+    rng = np.random.default_rng(seed)
+    rows = np.stack([np.zeros(n_rows, dtype=np.int64), rng.integers(0, N, n_rows),
+                     rng.integers(0, Hq, n_rows)], axis=1)
+    q, k, v = (x.float().numpy() for x in (inp.q, inp.k, inp.v))
+    t0 = time.perf_counter()
+    oracle.sdpa_rows(q, k, v, rows, inp.scale, True)
+    t = time.perf_counter() - t0
+    flops = float(np.sum(4.0 * d * (rows[:, 1] + 1)))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "blas": vendor,
+            "sample": "%d random (row, head) outputs of the N=16384 causal GQA prefill, each "
+                      "against its whole visible key range (%.2e FLOP, %.1f s)" % (n_rows, flops, t)}
 
-    def plain():
-        ea.paged_attn_decode(q, kc, vc, tab, ctx, max_context_len=mcl, scale=inp.scale,
-                             out=out, workspace=ws_plain)
 
-    def shared():
-        ea.paged_attn_decode_shared(q, kc, vc, tab, ctx, gs, pl, max_context_len=mcl,
-                                    max_group_size=mgs, max_prefix_len=mpl, scale=inp.scale,
-                                    out=out, workspace=ws_shared)
+def probe_lib():
+    """libattn_probes.so with argument types declared (built beside libattn.so)."""
+    import ctypes
+    from exact_attention_34_amd import build as _b
+    if not os.path.exists(_b.PROBE_LIB_PATH):
+        raise RuntimeError("libattn_probes.so is not built; run python -m exact_attention_34_amd.build")
+    L = ctypes.CDLL(_b.PROBE_LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    L.attn_probe_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    L.attn_probe_exp2.argtypes = [vp, i32, i32, vp]
+    L.attn_probe_random_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp, i32, vp]
+    for f in (L.attn_probe_mfma_bf16, L.attn_probe_exp2, L.attn_probe_random_read):
+        f.restype = i32
+    return L
+
+
+def achievable(dev, reps=10):
+    """What simple loops reach on this chip: the prefill's matrix op
+    (v_mfma_f32_32x32x16_bf16, independent chains, 4 waves per SIMD), the
+    softmax's exponential (v_exp_f32 chains) and 4 KiB reads at random block
+    ids (decode's access pattern: 2,048 waves, two blocks in flight each,
+    non-temporal), each timed over `reps` launches with HIP events."""
+    import ctypes
+    L = probe_lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
     def timed(fn):
-        for _ in range(5):
-            fn()
+        fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
@@ -243,24 +297,115 @@ def shared_decode(ea, workloads, dev, reps):
             fn()
         b.record()
         torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError("probe launch failed: hip error %d" % rc)
+
+    blocks, iters = 4096, 2000        # 4 waves per SIMD on 256 CUs
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t = timed(lambda: check(L.attn_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks,
+                                                     iters, stream)))
+    mfma = blocks * 4 * iters * 8 * 32768 / t / 1e12
+    t = timed(lambda: check(L.attn_probe_exp2(ctypes.c_void_p(out.data_ptr()), blocks, iters,
+                                              stream)))
+    exps = blocks * 256 * iters * 8 / t
+    nbytes = 1 << 30                  # 1 GiB of 4 KiB blocks, read in a random order
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    ids = torch.randperm(nbytes // 4096, generator=torch.Generator().manual_seed(3)).to(
+        torch.int32).to(dev)
+    waves = 2048
+    sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+    t = timed(lambda: check(L.attn_probe_random_read(
+        ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(ids.data_ptr()), ids.numel(),
+        ctypes.c_void_p(sink.data_ptr()), waves, stream)))
+    rd = nbytes / t / 1e9
+    del buf
+    return {
+        "mfma_bf16_TFLOPs": mfma, "exp2_per_s": exps, "random_4k_read_GBps": rd,
+        "note": "libattn_probes.so loops on this chip: independent v_mfma_f32_32x32x16_bf16 "
+                "chains (16,384 waves, varying operands); v_exp_f32 chains; 1 GiB read as "
+                "4 KiB blocks in random order by 2,048 waves with non-temporal loads",
+    }
+
+
+def shared_decode(ea, workloads, dev, reps):
+    """Per-sequence decode against sharing-aware decode on the shared-prefix
+    workload, timed with HIP events on the current stream over `reps` calls:
+    warm (the same pool, back-to-back calls) and cold (three pools of the same
+    shape -- seeds 5, 105, 205 -- used in turn, 604 MB of K/V against the
+    256 MB last-level cache, so a call finds little of its pool cached).
+    GB/s are reported on the logical bytes (what a per-sequence kernel reads)
+    and on the unique bytes (each shared block once)."""
+    pools = []
+    for seed in (5, 105, 205):
+        inp = workloads.decode_config5(seed=seed, nan_fill=True)
+        pools.append(dict(
+            inp=inp, q=inp.q.to(dev), kc=inp.k_cache.to(dev), vc=inp.v_cache.to(dev),
+            tab=inp.block_table.to(dev), ctx=inp.context_lens.to(dev),
+            gs=inp.group_starts.to(dev), pl=inp.prefix_lens.to(dev)))
+    inp = pools[0]["inp"]
+    S, Hq, d = inp.q.shape
+    Hkv = inp.k_cache.shape[1]
+    G = inp.prefix_lens.shape[0]
+    mcl = inp.max_context_len
+    mgs = int(np.diff(inp.group_starts.numpy()).max())
+    mpl = int(inp.prefix_lens.max())
+    out = torch.empty_like(pools[0]["q"])
+    ws_plain = torch.empty(ea.paged_attn_decode_workspace_size(S, Hq, Hkv, d, mcl),
+                           dtype=torch.uint8, device=dev)
+    ws_shared = torch.empty(ea.paged_attn_decode_shared_workspace_size(S, G, mgs, Hq, Hkv, d,
+                                                                       mcl, mpl),
+                            dtype=torch.uint8, device=dev)
+
+    def plain(P):
+        ea.paged_attn_decode(P["q"], P["kc"], P["vc"], P["tab"], P["ctx"], max_context_len=mcl,
+                             scale=inp.scale, out=out, workspace=ws_plain)
+
+    def shared(P):
+        ea.paged_attn_decode_shared(P["q"], P["kc"], P["vc"], P["tab"], P["ctx"], P["gs"],
+                                    P["pl"], max_context_len=mcl, max_group_size=mgs,
+                                    max_prefix_len=mpl, scale=inp.scale, out=out,
+                                    workspace=ws_shared)
+
+    def timed(fn, rotate):
+        for i in range(6):
+            fn(pools[i % 3 if rotate else 0])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            fn(pools[i % 3 if rotate else 0])
+        b.record()
+        torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    t_plain, t_shared = timed(plain), timed(shared)
+    warm_plain, warm_shared = timed(plain, False), timed(shared, False)
+    cold_plain, cold_shared = timed(plain, True), timed(shared, True)
     logical = workloads.decode_bytes(inp.context_lens.numpy(), Hkv, d)
     unique = workloads.decode_unique_bytes(inp.block_table.numpy(), inp.context_lens.numpy(),
                                            inp.block_size, Hkv, d)
+
+    def rates(t_plain, t_shared):
+        return {"per_sequence_ms": t_plain, "shared_ms": t_shared, "speedup": t_plain / t_shared,
+                "per_sequence_logical_GBps": logical / (t_plain * 1e-3) / 1e9,
+                "shared_logical_GBps": logical / (t_shared * 1e-3) / 1e9,
+                "shared_unique_GBps": unique / (t_shared * 1e-3) / 1e9,
+                "shared_unique_frac_of_hbm": unique / (t_shared * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
     return {
         "workload": "8 groups x 8 seqs, 4096-token shared prefix + 256-token private suffix, "
                     "Hq=32 Hkv=8 d=128 bf16 block 16 shuffled table",
-        "per_sequence_ms": t_plain, "shared_ms": t_shared, "speedup": t_plain / t_shared,
         "logical_bytes": logical, "unique_bytes": unique,
-        "shared_logical_GBps": logical / (t_shared * 1e-3) / 1e9,
-        "shared_unique_GBps": unique / (t_shared * 1e-3) / 1e9,
-        "shared_unique_frac_of_hbm": unique / (t_shared * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "note": "back-to-back calls.  The per-sequence call streams K/V past the caches "
-                "(non-temporal loads), so each sequence fetches the shared prefix again; the "
-                "sharing-aware call reads each prefix block once, with ordinary loads that can "
-                "hit the 256 MB last-level cache between calls",
+        "cold": rates(cold_plain, cold_shared),
+        "warm": rates(warm_plain, warm_shared),
+        "note": "cold: three pools of this shape used in turn (each call's 201 MB of unique "
+                "K/V was last read two calls, 402 MB, earlier); warm: one pool, back-to-back "
+                "calls.  The per-sequence call streams K/V past the caches (non-temporal loads), "
+                "so each sequence fetches the shared prefix again; the sharing-aware call reads "
+                "each prefix block once, with ordinary loads",
         "prefix_kernel_traffic": load_traffic("paged_decode_prefix_kernel"),
     }
 
@@ -433,6 +578,10 @@ def main():
               flush=True)
         return
 
+    if args.only == "probes":
+        print(json.dumps({"achievable": achievable(dev)}), flush=True)
+        return
+
     dec = workloads.decode_config4(nan_fill=True)
     dq = dec.q.to(dev)
     kc, vc = dec.k_cache.to(dev), dec.v_cache.to(dev)
@@ -445,27 +594,37 @@ def main():
     dec_bytes = workloads.decode_bytes(dec.context_lens.numpy(), 8, 128)
 
     run_pre = args.only in (None, "prefill")
+    run_long = args.only is None and not args.no_long
     run_dec = args.only in (None, "decode")
+    if run_long:
+        lpre = workloads.prefill_config(3)
+        lq, lk, lv = (x.to(dev) for x in (lpre.q, lpre.k, lpre.v))
+        lo = torch.empty_like(lq)
+        LB, LN, LHq, Ld = lq.shape
+        long_flops = workloads.prefill_flops(LB, LN, LN, LHq, Ld, True)
 
     def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
         if run_pre:
-            if ev is not None:
-                ev[0].record()
+            mark(0)
             ea.attn_fwd(q, k, v, causal=True, scale=pre.scale, out=o)
-            if ev is not None:
-                ev[1].record()
+            mark(1)
+        if run_long:
+            mark(2)
+            ea.attn_fwd(lq, lk, lv, causal=True, scale=lpre.scale, out=lo)
+            mark(3)
         if run_dec:
-            if ev is not None:
-                ev[2].record()
+            mark(4)
             ea.paged_attn_decode(dq, kc, vc, tab, ctx, max_context_len=mcl, scale=dec.scale,
                                  out=dout, workspace=ws)
-            if ev is not None:
-                ev[3].record()
+            mark(5)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -475,8 +634,13 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events])) if run_pre else None
-    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if run_dec else None
+
+    def mean_ms(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+
+    pre_ms = mean_ms(0, 1) if run_pre else None
+    long_ms = mean_ms(2, 3) if run_long else None
+    dec_ms = mean_ms(4, 5) if run_dec else None
 
     res = {
         "metric": METRIC,
@@ -487,11 +651,16 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {
             "workload": "causal prefill B=4 Hq=Hkv=16 N=2048 d=128 bf16 (1% Q/K rows x20) "
+                        "+ causal GQA prefill B=1 Hq=32 Hkv=8 N=16384 d=128 bf16 "
                         "+ paged decode 64 seqs ctx~U[512,8192] Hq=32 Hkv=8 d=128 bf16 "
                         "block 16 shuffled table",
             "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
         },
     }
+    ach = None
+    if args.only is None and not args.no_probes:
+        ach = achievable(dev)
+        res["achievable"] = ach
     if run_pre:
         tflops = pre_flops / (pre_ms * 1e-3) / 1e12
         traffic = load_traffic("attn_fwd_mfma_kernel")
@@ -499,7 +668,22 @@ def main():
         res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                            "traffic": traffic, "kernel": "attn_fwd_mfma_kernel<bf16,128,causal>",
+                           "workload": "causal prefill B=4 Hq=Hkv=16 N=2048 d=128 bf16",
                            "flop_per_launch": pre_flops, "mean_ms": pre_ms}
+        if ach:
+            res["roofline"]["frac_of_achievable"] = tflops / ach["mfma_bf16_TFLOPs"]
+    if run_long:
+        ltf = long_flops / (long_ms * 1e-3) / 1e12
+        res["long_prefill"] = {
+            "workload": "causal GQA prefill B=1 Hq=32 Hkv=8 N=16384 d=128 bf16",
+            "value": ltf, "unit": "TFLOP/s", "mean_ms": long_ms, "flop_per_launch": long_flops,
+            "roofline": {"bound": "mfma", "achieved": ltf, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ltf / PEAK_BF16_TFLOPS,
+                         "traffic": load_traffic("attn_fwd_mfma_kernel_long"),
+                         "kernel": "attn_fwd_mfma_kernel<bf16,128,causal>"},
+        }
+        if ach:
+            res["long_prefill"]["roofline"]["frac_of_achievable"] = ltf / ach["mfma_bf16_TFLOPs"]
     if run_dec:
         gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
         res["decode"] = {
@@ -510,12 +694,16 @@ def main():
                          "kernel": "paged_decode_split_kernel + paged_decode_combine_kernel",
                          "bytes_per_launch": dec_bytes},
         }
+        if ach:
+            res["decode"]["roofline"]["frac_of_achievable"] = gbs / ach["random_4k_read_GBps"]
     if args.only is None and not args.no_shared:
         res["shared_decode"] = shared_decode(ea, workloads, dev, args.steps)
         res["backward"] = backward(ea, pre, q, k, v, pre_flops, args.steps)
         res["paged_kv"] = paged_kv(ea, pre, q, k, v, pre_flops, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre, dec, dec_bytes, pre_flops)
+        if run_long:
+            res["long_prefill"]["cpu_baseline"] = long_prefill_cpu_baseline(lpre)
     print(json.dumps(res), flush=True)
 
 

@@ -37,3 +37,15 @@ def test_bench_prints_one_contract_line():
     assert 0 < dec["frac"] < 1
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["blas"]
+    # the N = 16384 prefill is timed in the same step, with its own roofline
+    # and an oracle baseline on sampled rows
+    lp = d["long_prefill"]
+    assert lp["value"] > 0 and lp["roofline"]["peak"] == 2500.0
+    assert abs(lp["roofline"]["frac"] - lp["value"] / 2500.0) < 1e-9
+    assert lp["cpu_baseline"]["kind"] == "oracle" and lp["cpu_baseline"]["value"] > 0
+    ach = d["achievable"]
+    assert ach["mfma_bf16_TFLOPs"] > 0 and ach["random_4k_read_GBps"] > 0
+    assert 0 < roof["frac_of_achievable"] and 0 < dec["frac_of_achievable"]
+    sd = d["shared_decode"]
+    assert sd["cold"]["shared_ms"] > 0 and sd["warm"]["shared_ms"] > 0

@@ -13,7 +13,8 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
-FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+FIELDS = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+GRID_C2, GRID_C3 = 512 * 512, 2048 * 512
 
 
 def _counter_dir(tmp_path, name, rows):
@@ -22,9 +23,11 @@ def _counter_dir(tmp_path, name, rows):
     with open(d / "run_counter_collection.csv", "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=FIELDS)
         w.writeheader()
-        for i, (kernel, counter, value) in enumerate(rows):
-            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": kernel, "Counter_Name": counter,
-                        "Counter_Value": value})
+        for i, row in enumerate(rows):
+            kernel, counter, value = row[:3]
+            grid = row[3] if len(row) > 3 else 64
+            w.writerow({"Dispatch_Id": i + 1, "Grid_Size": grid, "Kernel_Name": kernel,
+                        "Counter_Name": counter, "Counter_Value": value})
     return str(tmp_path / name)
 
 
@@ -47,9 +50,14 @@ def test_traffic_scaled_by_copy_calibration_and_gated_by_source_hash(tmp_path, m
     # averaged
     cf = _counter_dir(tmp_path, "cf", [(copy, "FETCH_SIZE", 524288.0)] * 3)
     cw = _counter_dir(tmp_path, "cw", [(copy, "WRITE_SIZE", 1048576.0)] * 3)
-    mf = _counter_dir(tmp_path, "mf", [(fwd, "FETCH_SIZE", 100.0), (fwd, "FETCH_SIZE", 300.0),
+    # the two prefills of the step are one kernel, told apart by their grids
+    mf = _counter_dir(tmp_path, "mf", [(fwd, "FETCH_SIZE", 100.0, GRID_C2),
+                                       (fwd, "FETCH_SIZE", 9000.0, GRID_C3),
+                                       (fwd, "FETCH_SIZE", 300.0, GRID_C2),
                                        (split, "FETCH_SIZE", 1000.0), (comb, "FETCH_SIZE", 10.0)])
-    mw = _counter_dir(tmp_path, "mw", [(fwd, "WRITE_SIZE", 50.0), (fwd, "WRITE_SIZE", 50.0),
+    mw = _counter_dir(tmp_path, "mw", [(fwd, "WRITE_SIZE", 50.0, GRID_C2),
+                                       (fwd, "WRITE_SIZE", 700.0, GRID_C3),
+                                       (fwd, "WRITE_SIZE", 50.0, GRID_C2),
                                        (split, "WRITE_SIZE", 4.0), (comb, "WRITE_SIZE", 1.0)])
     bench.write_traffic(mf, mw, cf, cw)
     t = json.loads(out.read_text())
@@ -59,6 +67,9 @@ def test_traffic_scaled_by_copy_calibration_and_gated_by_source_hash(tmp_path, m
     assert e["fetch_bytes"] == 200 * 1024 * 2 and e["write_bytes"] == 50 * 1024
     assert e["bytes_per_launch"] == e["fetch_bytes"] + e["write_bytes"]
     assert t["paged_decode_split_kernel"]["bytes_per_launch"] == 1000 * 1024 * 2 + 4 * 1024
+    el = t["attn_fwd_mfma_kernel_long"]
+    assert el["dispatches"] == [1, 1]
+    assert el["fetch_bytes"] == 9000 * 1024 * 2 and el["write_bytes"] == 700 * 1024
     # kernels of runs that were not given are left out
     assert "paged_decode_prefix_kernel" not in t and "attn_bwd_dkdv_kernel" not in t
     # reported only while the kernel sources are the ones measured
