@@ -19,7 +19,7 @@ from . import build as _build
 
 __all__ = [
     "AttnError", "lib", "abi_version", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
-    "paged_attn_decode",
+    "paged_attn_decode", "paged_attn_decode_noalloc", "DECODE_SCRATCH_BYTES",
     "paged_attn_decode_workspace_size", "paged_attn_decode_shared",
     "paged_attn_decode_shared_workspace_size", "paged_kv_write", "paged_kv_copy_blocks",
     "attn_fwd_paged", "validate_paged_tables",
@@ -79,6 +79,9 @@ def lib():
     L.paged_attn_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, ctypes.c_size_t, vp]
+    L.paged_attn_decode_noalloc.restype = i32
+    L.paged_attn_decode_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp,
+                                            i32, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     L.paged_attn_decode_shared_workspace_size.restype = ctypes.c_size_t
     L.paged_attn_decode_shared_workspace_size.argtypes = [i32] * 8
     L.paged_attn_decode_shared.restype = i32
@@ -298,6 +301,32 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_contex
                                    S, Hq, Hkv, d, bs, block_table.shape[1], int(max_context_len),
                                    NB, float(scale), _ptr(workspace), ws_bytes,
                                    _stream(q.device))
+    _check(code)
+    if return_lse:
+        return out, lse
+    return out
+
+
+# ATTN_DECODE_SCRATCH_BYTES of include/attn.h: the scratch the library holds
+# per GPU for paged_attn_decode_noalloc
+DECODE_SCRATCH_BYTES = 40 << 20
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                              scale=None, out=None, lse=None, return_lse=False):
+    """:func:`paged_attn_decode` on the library's own device scratch (the C
+    ABI's paged_attn_decode_noalloc): the library call allocates nothing.
+    Pass ``out`` (and ``lse`` with ``return_lse``) preallocated to keep the
+    whole call free of allocation.  Calls that overlap on one GPU race (one
+    scratch per GPU); calls ordered on one stream are safe."""
+    scale, out, lse = _decode_common(q, k_cache, v_cache, block_table, context_lens, scale,
+                                     out, lse, return_lse)
+    S, Hq, d = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    code = lib().paged_attn_decode_noalloc(
+        _DTYPE_CODE[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(context_lens), _ptr(out), _ptr(lse), S, Hq, Hkv, d, bs, block_table.shape[1],
+        int(max_context_len), NB, float(scale), _stream(q.device))
     _check(code)
     if return_lse:
         return out, lse

@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libattn_probes.so")
 SOURCES = ["attn_api.hip", "prefill.hip", "decode.hip", "backward.hip", "kv_cache.hip",
-           "block_manager.cpp", "validate.cpp"]
+           "scratch.hip", "block_manager.cpp", "validate.cpp"]
 PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

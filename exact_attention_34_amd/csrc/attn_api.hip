@@ -21,6 +21,8 @@ hipError_t launch_backward(int dtype, int head_dim, bool causal, const BwdParams
 hipError_t launch_decode_shared(int dtype, const DecodeParams& p, int64_t items,
                                 int max_context_len, hipStream_t stream);
 size_t decode_workspace_bytes(int num_seqs, int h_q, int h_kv, int head_dim, int max_context_len);
+size_t scratch_capacity();
+hipError_t scratch_address(int device, void** out);
 int decode_waves(int num_seqs, int h_kv, int max_context_len);
 SharedPlan shared_plan(int num_groups, int max_group_size, int h_q, int h_kv, int max_prefix_len);
 struct KvWriteParams {
@@ -557,12 +559,15 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int h_q, int h_kv, int hea
 
 namespace {
 
-// paged_attn_decode.
+// paged_attn_decode and its variant on the library's scratch.  With
+// workspace == nullptr and use_scratch set, the workspace is the scratch
+// array of the stream's device (sizes beyond it are rejected first).
 int decode_call(const char* fn, int dtype, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* block_table, const int32_t* context_lens,
                 void* o, float* lse, int num_seqs, int h_q, int h_kv, int head_dim,
                 int block_size, int max_blocks_per_seq, int max_context_len, int num_blocks,
-                float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                float softmax_scale, void* workspace, size_t workspace_bytes, bool use_scratch,
+                void* stream) {
   try {
     g_last_error.clear();
     attn::DecodeParams p;
@@ -571,6 +576,24 @@ int decode_call(const char* fn, int dtype, const void* q, const void* k_cache,
                           max_context_len, num_blocks, softmax_scale, p);
     if (rc != ATTN_OK || num_seqs == 0) return rc;
     const size_t need = attn::decode_workspace_bytes(num_seqs, h_q, h_kv, head_dim, max_context_len);
+    if (use_scratch) {
+      const size_t cap = attn::scratch_capacity();
+      if (need > cap)
+        return fail(ATTN_ERR_WORKSPACE, std::string(fn) + ": these sizes need " +
+                                            std::to_string(need) + " bytes of scratch; the "
+                                            "library holds " + std::to_string(cap));
+      if (need > 0) {
+        int dev = -1;
+        hipError_t e = stream != nullptr
+                           ? hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev)
+                           : hipGetDevice(&dev);
+        if (e == hipSuccess) e = attn::scratch_address(dev, &workspace);
+        if (e != hipSuccess)
+          return fail(ATTN_ERR_HIP, std::string(fn) + ": scratch lookup failed: " +
+                                        hipGetErrorString(e));
+        workspace_bytes = cap;
+      }
+    }
     rc = check_workspace(fn, workspace, workspace_bytes, need);
     if (rc != ATTN_OK) return rc;
     if (need > 0) {
@@ -580,7 +603,7 @@ int decode_call(const char* fn, int dtype, const void* q, const void* k_cache,
       p.ws_ml = p.ws_o + slots * head_dim;
       p.ws_unit = reinterpret_cast<int32_t*>(p.ws_ml + slots * 2);
     }
-    if (validate_enabled()) {
+    if (!use_scratch && validate_enabled()) {
       rc = validate_on_host(fn, reinterpret_cast<hipStream_t>(stream),
                             block_table, context_lens, num_seqs, max_blocks_per_seq,
                             max_context_len, num_blocks, block_size, nullptr, nullptr, 0);
@@ -612,7 +635,18 @@ int paged_attn_decode(int dtype, const void* q, const void* k_cache, const void*
   return decode_call("paged_attn_decode", dtype, q, k_cache, v_cache, block_table, context_lens,
                      o, lse, num_seqs, h_q, h_kv, head_dim, block_size, max_blocks_per_seq,
                      max_context_len, num_blocks, softmax_scale, workspace, workspace_bytes,
-                     stream);
+                     false, stream);
+}
+
+int paged_attn_decode_noalloc(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens, void* o,
+                              float* lse, int num_seqs, int h_q, int h_kv, int head_dim,
+                              int block_size, int max_blocks_per_seq, int max_context_len,
+                              int num_blocks, float softmax_scale, void* stream) {
+  return decode_call("paged_attn_decode_noalloc", dtype, q, k_cache, v_cache, block_table,
+                     context_lens, o, lse, num_seqs, h_q, h_kv, head_dim, block_size,
+                     max_blocks_per_seq, max_context_len, num_blocks, softmax_scale, nullptr, 0,
+                     true, stream);
 }
 
 size_t paged_attn_decode_shared_workspace_size(int num_seqs, int num_groups, int max_group_size,

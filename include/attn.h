@@ -262,6 +262,35 @@ int paged_attn_decode(int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, meaning and results as
+ * paged_attn_decode (the same kernels, bit for bit), without the workspace:
+ * the split-K partials go to a scratch array of ATTN_DECODE_SCRATCH_BYTES
+ * that the library holds in device memory, one per GPU, from the library's
+ * first use on that GPU until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a device
+ * looks up that device's scratch address once.
+ *
+ * Limits and sharing.  Sizes whose paged_attn_decode_workspace_size exceeds
+ * ATTN_DECODE_SCRATCH_BYTES are rejected with ATTN_ERR_WORKSPACE before
+ * anything is launched.  Every call on one GPU uses that GPU's one scratch
+ * array: calls that may overlap on the same GPU (different streams, or
+ * threads without ordering) race and give undefined results.  Calls ordered
+ * on one stream are safe; the scratch needs no clearing between them (its
+ * contents on entry do not matter, as for the workspace).  The ATTN_VALIDATE
+ * mode is not applied here (it copies to pageable host memory).
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)40 << 20)
+int paged_attn_decode_noalloc(int dtype,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              void* o, float* lse,
+                              int num_seqs, int h_q, int h_kv, int head_dim, int block_size,
+                              int max_blocks_per_seq, int max_context_len, int num_blocks,
+                              float softmax_scale, void* stream);
+
+/*
  * Bytes of device workspace paged_attn_decode_shared needs for these sizes
  * (the partials of both parts and a little per-sequence metadata).  Returns 0
  * for invalid sizes.

@@ -305,3 +305,19 @@ def test_validate_rejects_prefix_blocks_that_are_not_shared():
         a["block_table"][1, 0] = 3
     _rejects(r"block_table\[1\]\[0\] = 3 differs", mutate=mutate)
 
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
+    # 16 query heads per KV head over 65,535 sequences x 64 KV heads need
+    # more workspace than the library's scratch holds: rejected on the host,
+    # before any device call
+    need = ea.paged_attn_decode_workspace_size(65535, 1024, 64, 128, 1 << 20)
+    assert need > ea.DECODE_SCRATCH_BYTES
+    code = ea.lib().paged_attn_decode_noalloc(2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                              65535, 1024, 64, 128, 16, 1 << 16, 1 << 20, 1,
+                                              0.1, None)
+    assert code == 4, ea.lib().attn_last_error()
+    assert b"scratch" in ea.lib().attn_last_error()
+    # the capacity in the binding is the header's ATTN_DECODE_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert "#define ATTN_DECODE_SCRATCH_BYTES ((size_t)40 << 20)" in text
+    assert ea.DECODE_SCRATCH_BYTES == 40 << 20
