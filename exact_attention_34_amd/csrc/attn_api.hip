@@ -452,7 +452,8 @@ int paged_kv_copy_blocks(int dtype, void* k_cache, void* v_cache, const int32_t*
 
 size_t attn_bwd_workspace_size(int batch, int n_q, int h_q) {
   if (batch <= 0 || n_q <= 0 || h_q <= 0) return 0;
-  return align16((size_t)batch * h_q * n_q * 4);
+  // delta, then the log-sum-exp in log2 units, one fp32 each per query row
+  return 2 * align16((size_t)batch * h_q * n_q * 4);
 }
 
 int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
@@ -518,6 +519,8 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
     p.q = q; p.k = k; p.v = v; p.o = o; p.dout = d_o; p.lse = lse;
     p.dq = dq; p.dk = dk; p.dv = dv;
     p.delta = static_cast<float*>(workspace);
+    p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      align16((size_t)batch * h_q * n_q * 4));
     p.qs_b = q_stride[0]; p.qs_n = q_stride[1]; p.qs_h = q_stride[2];
     p.ks_b = k_stride[0]; p.ks_n = k_stride[1]; p.ks_h = k_stride[2];
     p.vs_b = v_stride[0]; p.vs_n = v_stride[1]; p.vs_h = v_stride[2];

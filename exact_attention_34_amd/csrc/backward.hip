@@ -13,7 +13,8 @@
 // needed the second time.
 //
 // Three kernels, none of them with atomics, so results are deterministic:
-//   * attn_bwd_delta_kernel: delta = rowsum(dO * O) per query row (fp32);
+//   * attn_bwd_delta_kernel: delta = rowsum(dO * O) per query row (fp32),
+//     and the forward log-sum-exp converted to log2 units;
 //   * attn_bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, KV head)
 //     and walks every query tile of every query head of the GQA group that
 //     can see them; dK and dV accumulate in registers (eight waves: 32 keys
@@ -69,7 +70,12 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
     for (int k = 0; k < 4; ++k) acc = TT::dot2(o[i][k], g[i][k], acc);
 #pragma unroll
     for (int sh = 1; sh < CPR; sh <<= 1) acc += __shfl_xor(acc, sh);
-    if (c == 0 && r < nrows) p.delta[((int64_t)b * p.h_q + h[i]) * p.n_q + n[i]] = acc;
+    if (c == 0 && r < nrows) {
+      const int64_t row = ((int64_t)b * p.h_q + h[i]) * p.n_q + n[i];
+      p.delta[row] = acc;
+      // the log-sum-exp in log2 units, as the probabilities are recomputed
+      p.lse2[row] = p.lse[row] * kLog2e;
+    }
   }
 }
 
@@ -97,33 +103,29 @@ __device__ inline int tswz(int r) {
 // lane 4 j + q points at row 4 (g / 2) + j and columns t*32 + 16 (g % 2) + 4 q
 // .. + 3; ds_read_b64_tr_b16 then leaves lane i with rows 4 (g / 2) .. + 3 of
 // column t*32 + 16 (g % 2) + i.  The second read of a 16-row k-step is 8 rows
-// further; those rows have another permutation, hence two offsets per block.
-// Adding 16 rows leaves the permutation unchanged.
+// further; adding 16 rows leaves the permutation unchanged.
+// tr_base gives block 0's first read; the others follow by flipping bits
+// (tr_ofs): block t changes only chunk bits 2..3, which move bits 5..6 of the
+// offset, and the rows 8 further have the permutation XOR 2 (chunk bit 1,
+// offset bit 4) and add 8 D, a bit that is clear in every first-read row.
+// Likewise the row read of k-step s is k-step 0's offset XOR 16 s.  So a
+// tile's offsets cost one XOR each from two per-lane values.
 template <int D>
-__device__ inline void tr_offsets(int lane, int (&ofs)[D / 32][2]) {
+__device__ inline int tr_base(int lane) {
   constexpr int CPR = D / 8;
   const int vi = lane & 15, vg = lane >> 4;
-  const int r0 = (vg >> 1) * 4 + (vi >> 2);
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int r = r0 + 8 * half;
-      const int el = t * 32 + (vg & 1) * 16 + (vi & 3) * 4;
-      ofs[t][half] = r * D + (((el >> 3) ^ tswz<CPR>(r)) * 8) + (el & 7);
-    }
+  const int r = (vg >> 1) * 4 + (vi >> 2);
+  const int el = (vg & 1) * 16 + (vi & 3) * 4;
+  return r * D + (((el >> 3) ^ tswz<CPR>(r)) * 8) + (el & 7);
 }
-
 template <int D>
-struct TrOfs {
-  int o[D / 32][2];   // block t, first / second read
-  __device__ inline int at(int t, int half) const { return o[t][half]; }
-};
+__device__ inline int tr_ofs(int base, int t, int half) {
+  return base ^ (32 * t) ^ (half ? (16 | 8 * D) : 0);
+}
+// Row-read offset of k-step 0 (row `row`, chunk `hi`).
 template <int D>
-__device__ inline TrOfs<D> tr_offsets2(int lane) {
-  TrOfs<D> r;
-  tr_offsets<D>(lane, r.o);
-  return r;
+__device__ inline int row_base(int row, int hi) {
+  return row * D + ((hi ^ tswz<D / 8>(row)) * 8);
 }
 
 // A operand of a 32x32x16 product whose k index runs over 16 rows of a tile
@@ -244,6 +246,11 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int per_head = nqt > qt0 ? nqt - qt0 : 0;
   const int ntiles = per_head * p.group;
 
+  // per-lane LDS offsets of k-step 0 and of transposing-read block 0; each
+  // tile derives its offsets from these with one XOR apiece
+  const int kbase0 = row_base<D>(rh * 32 + col, hi);
+  const int tbase0 = tr_base<D>(lane);
+
   // direct loads of the Q and dO tiles and of the tile's lse and delta rows
   const uint32_t qrowb = (uint32_t)p.qs_n * 2u, orowb = (uint32_t)p.dos_n * 2u;
   auto load_tile = [&](int idx, int stage) {
@@ -274,7 +281,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     if (wave == 0) {
       const int64_t row = ((int64_t)b * p.h_q + h) * p.n_q + q0;
       const uint32_t nb = (uint32_t)(p.n_q - q0) * 4u;
-      buf_load4_lds(make_rsrc(p.lse + row, nb), &lse_lds[stage][0], (uint32_t)lane * 4u);
+      buf_load4_lds(make_rsrc(p.lse2 + row, nb), &lse_lds[stage][0], (uint32_t)lane * 4u);
       buf_load4_lds(make_rsrc(p.delta + row, nb), &dl_lds[stage][0], (uint32_t)lane * 4u);
     }
   };
@@ -290,14 +297,13 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     const uint16_t* ob = o_lds + S * TILE;
     // rows whose visible keys do not cover this wave's keys need the mask
     const bool need_mask = CAUSAL && (q0 + off < k0 + kw * 32 + 31);
-    // LDS read offsets, computed here rather than held across the loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    // LDS read offsets, derived here rather than held across the loop (the
+    // empty statement keeps the compiler from hoisting them)
+    int kb0 = kbase0, tb0 = tbase0;
+    asm volatile("" : "+v"(kb0), "+v"(tb0));
     int kofs[NS];   // row reads: row col of this wave's 32 query rows, chunk 2 s + hi
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kofs[s] = (rh * 32 + (ln & 31)) * D + (((2 * s + (ln >> 5)) ^ tswz<CPR>(ln & 31)) * 8);
-    const TrOfs<D> tofs = tr_offsets2<D>(ln);
+    for (int s = 0; s < NS; ++s) kofs[s] = kb0 ^ (16 * s);
     // V rows of this wave's keys: the Q row offsets moved by (kw - rh) 32 rows
     const uint16_t* vb = v_lds + (kw - rh) * 32 * D;
     // One matrix product per slot, its LDS operand fetched PFD slots ahead:
@@ -310,7 +316,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     auto fetch = [&](int i) -> u32x4 {
       if (i < NSD) return *(const u32x4*)(((i & 1) ? ob : qb) + kofs[i >> 1]);
       const int j = i - NSD, ks = j / (2 * DT), t = (j >> 1) % DT;
-      return tr_operand(((j & 1) ? qb : ob) + (rh * 2 + ks) * 16 * D, tofs.at(t, 0), tofs.at(t, 1));
+      return tr_operand(((j & 1) ? qb : ob) + (rh * 2 + ks) * 16 * D, tr_ofs<D>(tb0, t, 0),
+                        tr_ofs<D>(tb0, t, 1));
     };
     // the B operand of a dP slot (V rows), fetched with its A operand
     auto fetch_v = [&](int i) -> u32x4 {
@@ -335,27 +342,36 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         sacc = TT::mma32(opnd[i], kf[i >> 1], sacc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane: key kcol, query rows q0 + 8 j + 4 hi + i (register 4 j + i)
+    // lane: key kcol, query rows q0 + 8 j + 4 hi + i (register 4 j + i);
+    // P = 2^(S c - lse log2 e) with the log-sum-exp stored in log2 units.
+    // Tiles whose keys every row of the wave sees skip the mask (the choice
+    // is uniform per wave).
     u32x4 pp[2], ps[2];
+    auto probs = [&](auto MC) {
+      constexpr bool MASK = decltype(MC)::value != 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 lv = *(const f32x4*)(&lse_lds[S][rh * 32 + 8 * j + 4 * hi]);
-      const f32x4 dl = *(const f32x4*)(&dl_lds[S][rh * 32 + 8 * j + 4 * hi]);
-      float pv[4], dsv[4];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 lv = *(const f32x4*)(&lse_lds[S][rh * 32 + 8 * j + 4 * hi]);
+        const f32x4 dl = *(const f32x4*)(&dl_lds[S][rh * 32 + 8 * j + 4 * hi]);
+        float pv[4], dsv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * j + i;
-        const int q = q0 + 8 * j + 4 * hi + i;
-        const bool vis = !need_mask || kcol <= q + off;
-        pv[i] = vis ? fast_exp2(fmaf(sacc[r], c, -lv[i] * kLog2e)) : 0.f;
-        dsv[i] = pv[i] * (dpacc[r] - dl[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          const float e = fast_exp2(fmaf(sacc[r], c, -lv[i]));
+          pv[i] = (!MASK || kcol <= q0 + 8 * j + 4 * hi + i + off) ? e : 0.f;
+          dsv[i] = pv[i] * (dpacc[r] - dl[i]);
+        }
+        // k-step j / 2 of the 32 query rows, values 4 (j % 2) .. + 3
+        pp[j >> 1][(j & 1) * 2 + 0] = TT::pack2(pv[0], pv[1]);
+        pp[j >> 1][(j & 1) * 2 + 1] = TT::pack2(pv[2], pv[3]);
+        ps[j >> 1][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
+        ps[j >> 1][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
       }
-      // k-step j / 2 of the 32 query rows, values 4 (j % 2) .. + 3
-      pp[j >> 1][(j & 1) * 2 + 0] = TT::pack2(pv[0], pv[1]);
-      pp[j >> 1][(j & 1) * 2 + 1] = TT::pack2(pv[2], pv[3]);
-      ps[j >> 1][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
-      ps[j >> 1][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
-    }
+    };
+    if (need_mask)
+      probs(IntC<1>());
+    else
+      probs(IntC<0>());
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end)
 #pragma unroll
@@ -469,9 +485,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
   float lse2 = 0.f, dl = 0.f;
   if (qvalid) {
     const int64_t row = ((int64_t)b * p.h_q + h) * p.n_q + qrow;
-    lse2 = p.lse[row] * kLog2e;
+    lse2 = p.lse2[row];
     dl = p.delta[row];
   }
+  // per-lane LDS offsets of k-step 0 and of transposing-read block 0
+  const int kbase0 = row_base<D>(col, hi);
+  const int tbase0 = tr_base<D>(lane);
   f32x16 dq[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -514,14 +533,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const uint16_t* vb = vst(S);
     const int k0 = kt * BN;
     const bool need_mask = (k0 + BN > p.n_k) || (CAUSAL && (k0 + BN - 1 > q0 + off));
-    // LDS read offsets, computed here rather than held across the loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    int kofs[NS];   // row reads: key row (ln % 32), chunk 2 s + ln / 32
+    // LDS read offsets, derived here rather than held across the loop
+    int kb0 = kbase0, tb0 = tbase0;
+    asm volatile("" : "+v"(kb0), "+v"(tb0));
+    int kofs[NS];   // row reads: key row (lane % 32), chunk 2 s + lane / 32
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kofs[s] = (ln & 31) * D + (((2 * s + (ln >> 5)) ^ tswz<CPR>(ln & 31)) * 8);
-    const TrOfs<D> tofs = tr_offsets2<D>(ln);
+    for (int s = 0; s < NS; ++s) kofs[s] = kb0 ^ (16 * s);
     // One matrix product per slot, its LDS operand fetched PFD slots ahead:
     // for each 32-key half, S^T = K Q^T and dP^T = V dO^T alternate over
     // the k-steps (then that half's dS^T is formed); then dQ^T += K^T dS^T
@@ -535,7 +552,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
         return *(const u32x4*)(((j & 1) ? vb : kb) + sub * 32 * D + kofs[j >> 1]);
       }
       const int j = i - 2 * NSD, ks = j / DT, t = j % DT;
-      return tr_operand(kb + ks * 16 * D, tofs.at(t, 0), tofs.at(t, 1));
+      return tr_operand(kb + ks * 16 * D, tr_ofs<D>(tb0, t, 0), tr_ofs<D>(tb0, t, 1));
     };
     u32x4 opnd[NSLOT];
 #pragma unroll
@@ -556,21 +573,29 @@ void attn_bwd_dq_kernel(BwdParams p) {
           sacc = TT::mma32(opnd[i], qf[j >> 1], sacc);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // lane: query qrow, keys k0 + sub*32 + 8 j + 4 hi + i (register 4 j + i)
+      // lane: query qrow, keys k0 + sub*32 + 8 j + 4 hi + i (register 4 j + i);
+      // tiles inside every row's visible range skip the mask (uniform choice)
+      auto grads = [&](auto MC) {
+        constexpr bool MASK = decltype(MC)::value != 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float dsv[4];
+        for (int j = 0; j < 4; ++j) {
+          float dsv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const int key = k0 + sub * 32 + 8 * j + 4 * hi + i;
-          const bool vis = !need_mask || (key < p.n_k && (!CAUSAL || key <= qrow + off));
-          const float pv = vis ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
-          dsv[i] = pv * (dpacc[r] - dl);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            const int key = k0 + sub * 32 + 8 * j + 4 * hi + i;
+            const float e = fast_exp2(fmaf(sacc[r], c, -lse2));
+            const bool vis = !MASK || (key < p.n_k && (!CAUSAL || key <= qrow + off));
+            dsv[i] = (vis ? e : 0.f) * (dpacc[r] - dl);
+          }
+          dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
+          dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
         }
-        dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 0] = TT::pack2(dsv[0], dsv[1]);
-        dsb[sub * 2 + (j >> 1)][(j & 1) * 2 + 1] = TT::pack2(dsv[2], dsv[3]);
-      }
+      };
+      if (need_mask)
+        grads(IntC<1>());
+      else
+        grads(IntC<0>());
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll

@@ -234,6 +234,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;       // [B][Hq][Nq] workspace: rowsum(dO * O)
+  float* lse2;        // [B][Hq][Nq] workspace: lse * log2(e)
   int64_t qs_b, qs_n, qs_h;
   int64_t ks_b, ks_n, ks_h;
   int64_t vs_b, vs_n, vs_h;

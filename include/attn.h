@@ -150,8 +150,9 @@ int attn_fwd(int dtype,
              float softmax_scale, int causal, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs (one fp32 per query row and head).
- * Returns 0 for empty or invalid sizes.
+ * Bytes of device workspace attn_bwd needs (two fp32 per query row and head:
+ * rowsum(dO * O) and the log-sum-exp in log2 units).  Returns 0 for empty or
+ * invalid sizes.
  */
 size_t attn_bwd_workspace_size(int batch, int n_q, int h_q);
 

@@ -229,8 +229,10 @@ def test_attn_bwd_empty_is_noop():
 def test_attn_bwd_workspace_size():
     L = ea.lib()
     assert L.attn_bwd_workspace_size(0, 128, 4) == 0
-    assert L.attn_bwd_workspace_size(2, 100, 3) == 2 * 100 * 3 * 4 + 0   # 2400 = 16 * 150
-    assert L.attn_bwd_workspace_size(1, 5, 1) == 32                      # 20 rounded up to 16
+    # two fp32 per query row (delta, log-sum-exp in log2 units), each array
+    # rounded up to 16 bytes
+    assert L.attn_bwd_workspace_size(2, 100, 3) == 2 * (2 * 100 * 3 * 4)   # 2400 = 16 * 150
+    assert L.attn_bwd_workspace_size(1, 5, 1) == 2 * 32                     # 20 rounded up to 32
 
 
 def test_last_error_cleared_on_success():
