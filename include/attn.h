@@ -29,9 +29,11 @@
  * inputs: fp32 throughout.
  *
  * Ownership.  Every pointer is device memory owned by the caller.  The
- * library never allocates or frees device memory, keeps no pointer after a
- * call returns, and holds no mutable global state apart from a thread-local
- * error message.  Calls are re-entrant.
+ * library never allocates or frees device memory and keeps no pointer after a
+ * call returns.  Its mutable global state is a thread-local error message and,
+ * for paged_attn_decode_noalloc only, one scratch array per GPU (a static
+ * device array of the code object, ATTN_DECODE_SCRATCH_BYTES) with its looked-up
+ * address.  Calls other than paged_attn_decode_noalloc are re-entrant.
  *
  * Asynchrony.  Calls only enqueue kernels on the given stream (a hipStream_t
  * passed as void*; NULL means the null stream) and never synchronise.  A
