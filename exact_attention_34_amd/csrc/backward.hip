@@ -188,15 +188,21 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int TILE = BQ * D;            // elements of a Q or dO tile
   constexpr int LOADS = BQ * CPR / NT;    // direct loads per thread per tile
   static_assert(LOADS * NT == BQ * CPR, "tile split");
-  // [Q stage 0][Q stage 1][dO stage 0][dO stage 1]; reused at the end for the
-  // partial sums (4 key groups x 32 keys x D fp32 = 64 KiB at D = 128) and
-  // the output staging
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * TILE];
+  // One array per stage (Q, dO, log-sum-exp and delta rows), named at compile
+  // time, so that the compiler can see that the stage being read is not the
+  // one the direct loads are filling; with a runtime stage index into one
+  // array it waits for the next tile's loads before the first read of every
+  // tile.  The four tile arrays are reused at the end for the partial sums
+  // and the output staging, one per key group.
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];   // this tile's V, [key][d]
-  __shared__ __attribute__((aligned(16))) float lse_lds[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dl_lds[2][BQ];
-  uint16_t* q_lds = tiles;
-  uint16_t* o_lds = tiles + 2 * TILE;
+  __shared__ __attribute__((aligned(16))) float lse_lds0[BQ];
+  __shared__ __attribute__((aligned(16))) float lse_lds1[BQ];
+  __shared__ __attribute__((aligned(16))) float dl_lds0[BQ];
+  __shared__ __attribute__((aligned(16))) float dl_lds1[BQ];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -251,50 +257,66 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int kbase0 = row_base<D>(rh * 32 + col, hi);
   const int tbase0 = tr_base<D>(lane);
 
-  // direct loads of the Q and dO tiles and of the tile's lse and delta rows
+  // direct loads of the Q and dO tiles and of the tile's lse and delta rows.
+  // Load i of a wave covers rows (8 i + wave) RPI + lane / CPR, lane % CPR
+  // naming the LDS chunk; a row's swizzle depends on the row mod 16 alone,
+  // which does not change with i, so each lane's byte offset is fixed and
+  // the rest is a uniform offset per load.
+  constexpr int RPI = 64 / CPR;   // rows per load instruction
+  static_assert((8 * RPI) % 16 == 0, "a load index step keeps the row mod 16");
   const uint32_t qrowb = (uint32_t)p.qs_n * 2u, orowb = (uint32_t)p.dos_n * 2u;
-  auto load_tile = [&](int idx, int stage) {
+  auto load_tile = [&](int idx, auto SC) {
+    constexpr int ST = decltype(SC)::value;
+    // the lane's offsets, derived per tile (a few instructions) rather than
+    // held in registers across the loop: the empty statement hides the lane
+    // index from loop-invariant hoisting
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lrow = ln / CPR, lpc = ln % CPR;
+    const uint32_t cb = (uint32_t)((lpc ^ tswz<CPR>(wave * RPI + lrow)) * 16);
+    const uint32_t vq = (uint32_t)lrow * qrowb + cb, vo = (uint32_t)lrow * orowb + cb;
+    uint16_t* qd = ST ? q_lds1 : q_lds0;
+    uint16_t* od = ST ? o_lds1 : o_lds0;
     const int h = kvh * p.group + idx / per_head;
     const int q0 = (qt0 + idx % per_head) * BQ;
     const T* Qg = (const T*)p.q + (int64_t)b * p.qs_b + (int64_t)h * p.qs_h;
     const T* Og = (const T*)p.dout + (int64_t)b * p.dos_b + (int64_t)h * p.dos_h;
     const uint32_t oq = (uint32_t)q0 * qrowb, oo = (uint32_t)q0 * orowb;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(
-        (const char*)Qg + oq, __builtin_amdgcn_readfirstlane(p.q_bytes > oq ? p.q_bytes - oq : 0u));
+        uniform_ptr((const char*)Qg + oq),
+        __builtin_amdgcn_readfirstlane(p.q_bytes > oq ? p.q_bytes - oq : 0u));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-        (const char*)Og + oo, __builtin_amdgcn_readfirstlane(p.do_bytes > oo ? p.do_bytes - oo : 0u));
-    // offsets recomputed per tile (a few instructions) instead of held in
-    // registers across the loop: the empty statement hides the lane index
-    // from loop-invariant hoisting
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+        uniform_ptr((const char*)Og + oo),
+        __builtin_amdgcn_readfirstlane(p.do_bytes > oo ? p.do_bytes - oo : 0u));
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int slot = (i * 8 + wave) * 64 + ln;
-      const int row = slot / CPR, pc = slot % CPR;
-      const uint32_t cb = (uint32_t)((pc ^ tswz<CPR>(row)) * 16);
-      buf_load16_lds(rq, q_lds + stage * TILE + (i * 8 + wave) * 512, (uint32_t)row * qrowb + cb);
-      buf_load16_lds(ro, o_lds + stage * TILE + (i * 8 + wave) * 512, (uint32_t)row * orowb + cb);
+      const uint32_t r0 = (uint32_t)((i * 8 + wave) * RPI);
+      buf_load16_lds(rq, qd + (i * 8 + wave) * 512, vq, r0 * qrowb);
+      buf_load16_lds(ro, od + (i * 8 + wave) * 512, vo, r0 * orowb);
     }
     // rows past n_q read as zero: their Q and dO rows are zero too, so they
     // contribute nothing whatever their probabilities
     if (wave == 0) {
       const int64_t row = ((int64_t)b * p.h_q + h) * p.n_q + q0;
-      const uint32_t nb = (uint32_t)(p.n_q - q0) * 4u;
-      buf_load4_lds(make_rsrc(p.lse2 + row, nb), &lse_lds[stage][0], (uint32_t)lane * 4u);
-      buf_load4_lds(make_rsrc(p.delta + row, nb), &dl_lds[stage][0], (uint32_t)lane * 4u);
+      const uint32_t nb = __builtin_amdgcn_readfirstlane((uint32_t)(p.n_q - q0) * 4u);
+      buf_load4_lds(make_rsrc(uniform_ptr(p.lse2 + row), nb), ST ? lse_lds1 : lse_lds0,
+                    (uint32_t)lane * 4u);
+      buf_load4_lds(make_rsrc(uniform_ptr(p.delta + row), nb), ST ? dl_lds1 : dl_lds0,
+                    (uint32_t)lane * 4u);
     }
   };
 
-  if (ntiles > 0) load_tile(0, 0);
-  for (int idx = 0; idx < ntiles; ++idx) {
-    const int S = idx & 1;
+  // one query tile, read from stage S (tile idx lands in stage idx & 1)
+  auto step = [&](const int idx, auto SC) {
+    constexpr int S = decltype(SC)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // tile idx landed; every wave is done with stage S ^ 1
-    if (idx + 1 < ntiles) load_tile(idx + 1, S ^ 1);
+    if (idx + 1 < ntiles) load_tile(idx + 1, IntC<S ^ 1>());
     const int q0 = (qt0 + idx % per_head) * BQ + rh * 32;   // this wave's first row
-    const uint16_t* qb = q_lds + S * TILE;
-    const uint16_t* ob = o_lds + S * TILE;
+    const uint16_t* qb = S ? q_lds1 : q_lds0;
+    const uint16_t* ob = S ? o_lds1 : o_lds0;
+    const float* lsb = S ? lse_lds1 : lse_lds0;
+    const float* dlb = S ? dl_lds1 : dl_lds0;
     // rows whose visible keys do not cover this wave's keys need the mask
     const bool need_mask = CAUSAL && (q0 + off < k0 + kw * 32 + 31);
     // LDS read offsets, derived here rather than held across the loop (the
@@ -351,8 +373,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
       constexpr bool MASK = decltype(MC)::value != 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 lv = *(const f32x4*)(&lse_lds[S][rh * 32 + 8 * j + 4 * hi]);
-        const f32x4 dl = *(const f32x4*)(&dl_lds[S][rh * 32 + 8 * j + 4 * hi]);
+        const f32x4 lv = *(const f32x4*)(lsb + rh * 32 + 8 * j + 4 * hi);
+        const f32x4 dl = *(const f32x4*)(dlb + rh * 32 + 8 * j + 4 * hi);
         float pv[4], dsv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -384,21 +406,28 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         dv[t] = TT::mma32(opnd[i], pp[ks], dv[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  if (ntiles > 0) load_tile(0, IntC<0>());
+  for (int idx = 0; idx < ntiles; idx += 2) {
+    step(idx, IntC<0>());
+    if (idx + 1 < ntiles) step(idx + 1, IntC<1>());
   }
 
   // ---- epilogue: sum the two row halves of each key group, then write
   // dK = scale dK^T^T and dV = dV^T^T as whole rows through LDS ----
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();   // every wave is done with the tiles
-  float* part = (float*)tiles;   // [key group][t][4 floats of 16][lane][4]
-  static_assert(4 * (D / 32) * 16 * 64 * 4 <= 4 * TILE * 2, "partial sums fit");
+  // key group kw's region: one of the four tile arrays
+  uint16_t* region = kw == 0 ? q_lds0 : kw == 1 ? q_lds1 : kw == 2 ? o_lds0 : o_lds1;
+  float* part = (float*)region;   // [t][4 floats of 16][lane][4]
+  static_assert((D / 32) * 16 * 64 * 4 <= TILE * 2, "partial sums fit");
   auto merge = [&](f32x16 (&acc)[D / 32]) {
     if (rh == 1) {
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          *(f32x4*)(part + (((kw * (D / 32) + t) * 4 + e) * 64 + lane) * 4) =
+          *(f32x4*)(part + ((t * 4 + e) * 64 + lane) * 4) =
               f32x4{acc[t][4 * e], acc[t][4 * e + 1], acc[t][4 * e + 2], acc[t][4 * e + 3]};
     }
     __syncthreads();
@@ -407,7 +436,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const f32x4 x = *(const f32x4*)(part + (((kw * (D / 32) + t) * 4 + e) * 64 + lane) * 4);
+          const f32x4 x = *(const f32x4*)(part + ((t * 4 + e) * 64 + lane) * 4);
 #pragma unroll
           for (int u = 0; u < 4; ++u) acc[t][4 * e + u] += x[u];
         }
@@ -417,8 +446,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   merge(dk);
   merge(dv);
   if (rh == 0) {
-    uint16_t* stage = tiles + kw * 32 * (D + 8);
-    static_assert(4 * 32 * (D + 8) <= 4 * TILE, "output staging fits");
+    uint16_t* stage = region;
+    static_assert(32 * (D + 8) <= TILE, "output staging fits");
     T* dKg = (T*)p.dk + (int64_t)b * p.dks_b + (int64_t)kvh * p.dks_h;
     T* dVg = (T*)p.dv + (int64_t)b * p.dvs_b + (int64_t)kvh * p.dvs_h;
     store_rows<TT, D>(dk, p.scale, stage, lane, dKg, p.dks_n, k0 + kw * 32, p.n_k);

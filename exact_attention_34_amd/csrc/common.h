@@ -188,6 +188,12 @@ __device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            off, 0, 0, 0);
 }
+// The same with a wave-uniform byte offset `soff` added to every lane's.
+__device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           off, soff, 0, 0);
+}
 // 4 bytes per lane straight into LDS: the wave fills 256 consecutive bytes.
 __device__ inline void buf_load4_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
