@@ -35,7 +35,9 @@ Prints one JSON line:
 With --only long, the long causal GQA prefill alone, timed over back-to-back
 calls, as {"long_prefill": ...}; --only probes runs the achievable-peak
 probes alone.
-Kernel times come from HIP events recorded on the stream the kernels run on.
+Kernel times come from HIP events recorded on the stream the kernels run on;
+the step's per-launch events skip the system-scope cache write-back that a
+default event makes before its timestamp (LaunchEvent).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB copies, for counters
@@ -187,6 +189,56 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, sfetch_d
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+class LaunchEvent:
+    """A HIP event recorded on torch's current stream (the stream the library
+    launches on), created with hipEventDisableSystemFence.  A default event
+    makes a system-scope release before it takes its timestamp, which writes
+    the caches back after the kernel just timed: 1-2 us per launch that is
+    not the kernel's and that rocprofv3's kernel time does not include.  The
+    interface is torch.cuda.Event's record() / elapsed_time()."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+    @classmethod
+    def runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            hip = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch has loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self.runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+
+    def record(self):
+        rc = self.runtime().hipEventRecord(self.ev, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_time(self, other):
+        """Milliseconds from this event to `other` (both completed)."""
+        ms = self._ct.c_float()
+        rc = self.runtime().hipEventElapsedTime(self._ct.byref(ms), self.ev, other.ev)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
 
 
 def copy_calibration():
@@ -624,7 +676,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[LaunchEvent() for _ in range(6)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
