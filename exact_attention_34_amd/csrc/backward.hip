@@ -34,6 +34,26 @@
 namespace attn {
 
 // ----------------------------------------------------------------------------
+// work-item order
+// ----------------------------------------------------------------------------
+// Workgroup i runs on XCD i % 8.  The dK/dV and dQ grids number their items
+// (tile rank, batch-head), the longest tiles first under the causal mask, so
+// each XCD gets the batch-heads equal to it mod 8.  When the batch-head count
+// is a multiple of 32, each XCD instead takes its batch-heads four at a time:
+// every tile of four batch-heads, longest first, before any tile of the next
+// four.  The tiles running together then read the Q/dO (or K/V) rows of four
+// batch-heads rather than of all of them, which the XCD's 4 MB L2 can hold,
+// and the longest-first order still holds within each group of four.  (All
+// of an XCD's tiles for two batch-heads at once halves the fetches too, but
+// mixes long and short tiles in every round and ran 10 % slower.)
+__device__ inline int group_heads_on_xcd(int blk, int bh, int ntile) {
+  if ((bh & 31) != 0) return blk;
+  const int x = blk & 7, pos = blk >> 3;
+  const int per = 4 * ntile, g = pos / per, w = pos - g * per;
+  return (w >> 2) * bh + (g * 4 + (w & 3)) * 8 + x;
+}
+
+// ----------------------------------------------------------------------------
 // delta = rowsum(dO * O)
 // ----------------------------------------------------------------------------
 // Rows are taken in (position, head) order, so that with the usual
@@ -210,7 +230,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int col = lane & 31, hi = lane >> 5;
   // items: key tile (the first tiles see the most queries when causal), batch, KV head
   const int bh = p.batch * p.h_kv;
-  const int kt = blockIdx.x / bh, rem = blockIdx.x - kt * bh;
+  const int blk = group_heads_on_xcd(blockIdx.x, bh, p.n_kt);
+  const int kt = blk / bh, rem = blk - kt * bh;
   const int b = rem / p.h_kv, kvh = rem - b * p.h_kv;
   const int k0 = kt * BK;
   const int kcol = k0 + kw * 32 + col;   // this lane's key
@@ -481,7 +502,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int col = lane & 31, hi = lane >> 5;
   // items: query tile (longest first when causal), batch, head
   const int bh = p.batch * p.h_q;
-  const int rank = blockIdx.x / bh, rem = blockIdx.x - rank * bh;
+  const int blk = group_heads_on_xcd(blockIdx.x, bh, p.n_qt);
+  const int rank = blk / bh, rem = blk - rank * bh;
   const int b = rem / p.h_q, h = rem - b * p.h_q;
   const int qt = CAUSAL ? (p.n_qt - 1 - rank) : rank;
   const int q0 = qt * BM;

@@ -140,6 +140,45 @@ def test_strided_views():
     _case(1, 190, 190, 2, 1, 128, "bf16", False, seed=95, strided=True)
 
 
+@pytest.mark.parametrize("shape", [
+    (2, 300, 300, 16, 16, 128, "bf16", True),    # 32 batch-heads in both kernels
+    (1, 200, 200, 32, 8, 128, "bf16", True),     # 32 query heads (dQ), 8 KV heads (dK/dV)
+    (4, 260, 260, 16, 16, 64, "f16", False),     # 64 batch-heads, d = 64
+], ids=["bh32", "gqa_hq32", "bh64_d64"])
+def test_head_groups_on_xcds(shape):
+    """Batch-head counts that are multiples of 32, where both kernels take
+    their items four batch-heads at a time per XCD."""
+    _case(*shape, seed=97 + shape[3])
+
+
+def test_full_scale_sampled_heads():
+    """The N=2048 causal workload (B=4, H=16, d=128 bf16, 1 % of Q/K rows x20)
+    in the benchmark's launch configuration, checked against the oracle on
+    four whole (batch, head) slices, one per group of four batch-heads of
+    different XCDs; every other gradient element is checked to be finite."""
+    inp = workloads.prefill_config(2)
+    B, N, H, d = inp.q.shape
+    rng = np.random.default_rng(7)
+    do = workloads._round(rng.standard_normal((B, N, H, d)), "bf16")
+    q, k, v, g = (x.to(DEV) for x in (inp.q, inp.k, inp.v, do))
+    print("case: full-scale B=%d N=%d H=%d d=%d bf16 causal" % (B, N, H, d), flush=True)
+    o, lse = ea.attn_fwd(q, k, v, causal=True, scale=inp.scale, return_lse=True)
+    dq, dk, dv = ea.attn_bwd(q, k, v, o, g, lse, causal=True, scale=inp.scale)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    for b, h in ((0, 0), (1, 5), (2, 10), (3, 15)):
+        sl = lambda x: x[b:b + 1, :, h:h + 1].double().numpy()
+        qn, kn, vn, gn = sl(inp.q), sl(inp.k), sl(inp.v), sl(do)
+        rq, rk, rv = oracle.sdpa_bwd(qn, kn, vn, gn, inp.scale, True)
+        o_ref, _ = oracle.sdpa(qn, kn, vn, inp.scale, True)
+        aq, ak, av = _abs_scale(qn, kn, vn, gn, o_ref, inp.scale, True)
+        what = "full-scale b=%d h=%d" % (b, h)
+        backward_gate(dq[b:b + 1, :, h:h + 1], rq, aq, torch.bfloat16, what + " dq")
+        backward_gate(dk[b:b + 1, :, h:h + 1], rk, ak, torch.bfloat16, what + " dk")
+        backward_gate(dv[b:b + 1, :, h:h + 1], rv, av, torch.bfloat16, what + " dv")
+
+
 def _random_cases(n, seed):
     """Seeded random backward problems: ragged sizes around the 64- and
     128-row tiles, GQA ratios 1..4, both head dims and dtypes, both masks,
