@@ -30,28 +30,9 @@
 // dQ^T = K^T dS^T.  The transposed operands (dO^T, Q^T, K^T) are read from
 // row-major LDS tiles with ds_read_b64_tr_b16.
 #include "common.h"
+#include "schedule.h"
 
 namespace attn {
-
-// ----------------------------------------------------------------------------
-// work-item order
-// ----------------------------------------------------------------------------
-// Workgroup i runs on XCD i % 8.  The dK/dV and dQ grids number their items
-// (tile rank, batch-head), the longest tiles first under the causal mask, so
-// each XCD gets the batch-heads equal to it mod 8.  When the batch-head count
-// is a multiple of 32, each XCD instead takes its batch-heads four at a time:
-// every tile of four batch-heads, longest first, before any tile of the next
-// four.  The tiles running together then read the Q/dO (or K/V) rows of four
-// batch-heads rather than of all of them, which the XCD's 4 MB L2 can hold,
-// and the longest-first order still holds within each group of four.  (All
-// of an XCD's tiles for two batch-heads at once halves the fetches too, but
-// mixes long and short tiles in every round and ran 10 % slower.)
-__device__ inline int group_heads_on_xcd(int blk, int bh, int ntile) {
-  if ((bh & 31) != 0) return blk;
-  const int x = blk & 7, pos = blk >> 3;
-  const int per = 4 * ntile, g = pos / per, w = pos - g * per;
-  return (w >> 2) * bh + (g * 4 + (w & 3)) * 8 + x;
-}
 
 // ----------------------------------------------------------------------------
 // delta = rowsum(dO * O)

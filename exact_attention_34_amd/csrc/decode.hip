@@ -33,6 +33,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "schedule.h"
 
 namespace attn {
 
@@ -50,26 +51,6 @@ __device__ inline int unit_blocks(int ctx, int fb) {
 }
 __device__ inline int first_block_of(const DecodeParams& p, int s) {
   return p.first_block != nullptr ? p.first_block[s] : 0;
-}
-
-// Waves that take part for a list of T blocks: every wave gets at least
-// kDecMinBlocks blocks (fewer waves, fewer units cut between them), at most
-// the W launched.
-constexpr int kDecMinBlocks = 8;
-__device__ inline int used_waves(int64_t T, int W) {
-  const int64_t w = (T + kDecMinBlocks - 1) / kDecMinBlocks;
-  return w < W ? (int)w : W;
-}
-
-// Range of wave w in the flattened block list: [w T / W, (w + 1) T / W).
-__device__ inline int64_t range_start(int w, int64_t T, int W) { return (int64_t)w * T / W; }
-
-// The wave whose range holds block b (0 <= b < T): the last w whose range
-// starts at or before b.
-__device__ inline int wave_of(int64_t b, int64_t T, int W) {
-  int w = (int)(b * W / T);   // range_start(w) <= b already
-  while (w + 1 < W && range_start(w + 1, T, W) <= b) ++w;
-  return w;
 }
 
 // Total unit blocks over all sequences and those of sequences before `s`,

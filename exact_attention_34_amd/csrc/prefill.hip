@@ -34,23 +34,9 @@
 // fp32 kernel: plain fp32 arithmetic on the vector ALUs (the fp32 matrix
 // rate equals the vector rate on this chip); four lanes share a query row.
 #include "common.h"
+#include "schedule.h"
 
 namespace attn {
-
-// ----------------------------------------------------------------------------
-// work-item mapping
-// ----------------------------------------------------------------------------
-// Workgroup i runs on XCD i % 8.  Items are numbered longest-first (query
-// tile descending when causal), then batch, then head; consecutive heads of a
-// GQA group are consecutive items.  With xcd_chunk = c > 0 (and num_items a
-// multiple of 8c), chunks of c consecutive items are dealt round-robin to the
-// XCDs, so the c workgroups of a chunk run on the same XCD and share its L2.
-__device__ inline int remap_item(int i, int num_items, int chunk) {
-  if (chunk <= 1 || (num_items % (8 * chunk)) != 0) return i;
-  const int x = i & 7, pos = i >> 3;
-  const int round = pos / chunk, within = pos - round * chunk;
-  return (round * 8 + x) * chunk + within;
-}
 
 // ----------------------------------------------------------------------------
 // 16-bit matrix-core kernel
