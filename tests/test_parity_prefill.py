@@ -93,8 +93,9 @@ def test_config3_long_causal_gqa_sampled():
 @pytest.mark.timeout(1200)
 def test_config3_long_causal_gqa_full():
     # every output row and log-sum-exp of the N = 16384 workload against the
-    # oracle (the launch the benchmark times: 1,024 work items of 256 rows,
-    # two query heads of a GQA group each, chunks of 2 items per XCD)
+    # oracle (the launch the benchmark times: 2,048 work items of 256 rows,
+    # 128 rows of each of two query heads of a GQA group, chunks of 2 items
+    # per XCD)
     inp = workloads.prefill_config(3)
     print("case: N=16384 Hq=32 Hkv=8 causal, all rows", flush=True)
     o, lse = _run(inp)
