@@ -45,9 +45,9 @@ namespace attn {
 // through each sequence's block table, its context length sets n_k, and the
 // n_q query rows are the last n_q tokens of that context.
 // NW waves per workgroup, 32 query rows each.  The workgroup's 32 NW rows
-// are p.hpw heads (of one KV head's group) x p.bm consecutive query rows; all
-// of them read the same K/V tiles, so each tile staged in LDS serves 32 NW
-// rows.
+// are p.hpw heads (of one KV head's group) x bm = 32 NW / p.hpw consecutive
+// query rows; all of them read the same K/V tiles, so each tile staged in LDS
+// serves 32 NW rows.
 template <typename TT, int D, bool CAUSAL, bool PAGED, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(FwdParams p) {
