@@ -52,7 +52,6 @@ default event makes before its timestamp (LaunchEvent).
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time

@@ -147,7 +147,6 @@ template <typename TT, int D>
 __device__ inline void store_rows(const f32x16 (&acc)[D / 32], float mul, uint16_t* stage,
                                   int lane, typename TT::elem* dst, int64_t stride, int row0,
                                   int n) {
-  typedef typename TT::elem T;
   constexpr int CPR = D / 8;
   constexpr int OP = D + 8;   // padded row, elements
   const int col = lane & 31, hi = lane >> 5;

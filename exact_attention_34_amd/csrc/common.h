@@ -199,9 +199,6 @@ __device__ inline void buf_load4_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
                                            off, 0, 0, 0);
 }
-__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
-}
 
 struct FwdParams {
   const void* q;
