@@ -51,31 +51,35 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   const T* Ob = (const T*)p.o + (int64_t)b * p.os_b + c * 8;
   const T* Gb = (const T*)p.dout + (int64_t)b * p.dos_b + c * 8;
   u32x4 o[PASSES], g[PASSES];
-  int n[PASSES], h[PASSES];
+  int64_t row[PASSES];
+  float lse[PASSES];
+  // every load of the thread (its O and dO chunks, and for the first lane of
+  // a row the row's log-sum-exp) is issued before any is used
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
     const int64_t r = ((int64_t)blockIdx.x * PASSES + i) * RPP + tid / CPR;
-    n[i] = (int)(r / p.h_q);
-    h[i] = (int)(r - (int64_t)n[i] * p.h_q);
+    const int n = (int)(r / p.h_q);
+    const int h = (int)(r - (int64_t)n * p.h_q);
+    row[i] = r < nrows ? ((int64_t)b * p.h_q + h) * p.n_q + n : -1;
     o[i] = g[i] = u32x4{0, 0, 0, 0};
+    lse[i] = 0.f;
     if (r < nrows) {
-      o[i] = *(const u32x4*)(Ob + (int64_t)n[i] * p.os_n + (int64_t)h[i] * p.os_h);
-      g[i] = *(const u32x4*)(Gb + (int64_t)n[i] * p.dos_n + (int64_t)h[i] * p.dos_h);
+      o[i] = *(const u32x4*)(Ob + (int64_t)n * p.os_n + (int64_t)h * p.os_h);
+      g[i] = *(const u32x4*)(Gb + (int64_t)n * p.dos_n + (int64_t)h * p.dos_h);
+      if (c == 0) lse[i] = p.lse[row[i]];
     }
   }
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
-    const int64_t r = ((int64_t)blockIdx.x * PASSES + i) * RPP + tid / CPR;
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc = TT::dot2(o[i][k], g[i][k], acc);
 #pragma unroll
     for (int sh = 1; sh < CPR; sh <<= 1) acc += __shfl_xor(acc, sh);
-    if (c == 0 && r < nrows) {
-      const int64_t row = ((int64_t)b * p.h_q + h[i]) * p.n_q + n[i];
-      p.delta[row] = acc;
+    if (c == 0 && row[i] >= 0) {
+      p.delta[row[i]] = acc;
       // the log-sum-exp in log2 units, as the probabilities are recomputed
-      p.lse2[row] = p.lse[row] * kLog2e;
+      p.lse2[row[i]] = lse[i] * kLog2e;
     }
   }
 }
