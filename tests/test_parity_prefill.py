@@ -58,6 +58,15 @@ def test_config2_causal_stress_full():
     _check_full(inp, "B=4 H=16 N=2048 d=128 bf16 causal, stress rows x20")
 
 
+def test_config2_shape_fp16_full():
+    """The N=2048 workload's shapes and x20 stress rows in fp16 (the f16
+    matrix-core path at full size), every output against the oracle."""
+    c = dict(workloads.PREFILL_CONFIGS[2])
+    c["dtype"] = "f16"
+    _check_full(workloads.prefill_inputs(seed=12, **c),
+                "B=4 H=16 N=2048 d=128 f16 causal, stress rows x20")
+
+
 def test_config3_long_causal_gqa_sampled():
     inp = workloads.prefill_config(3)
     print("case: N=16384 Hq=32 Hkv=8 causal, sampled rows", flush=True)
