@@ -46,6 +46,17 @@ def test_config4_full(config4):
     _check(config4, "64 seqs ctx U[512,8192] 32/8 heads shuffled table")
 
 
+def test_config4_shapes_fp16():
+    """The 64-sequence workload's context lengths and heads with fp16 K/V (the
+    f16 matrix-core path of the split kernel at full size)."""
+    c = workloads.DECODE_CONFIGS[4]
+    ctx = np.random.default_rng(4).integers(c["ctx_lo"], c["ctx_hi"], size=c["num_seqs"],
+                                            endpoint=True)
+    inp = workloads.decode_inputs(ctx, c["h_q"], c["h_kv"], c["d"], c["block_size"], "f16", 44,
+                                  max_blocks_per_seq=c["ctx_hi"] // c["block_size"])
+    _check(inp, "64 seqs ctx U[512,8192] 32/8 heads shuffled table, fp16")
+
+
 def test_config4_identity_layout_bitwise(config4):
     # the same logical sequences laid out contiguously (identity block order)
     out1, lse1 = _run(config4)

@@ -99,6 +99,28 @@ def test_config3_long_causal_gqa_sampled():
         assert (of[:, :, h, :] <= vmax[:, None, h // g, :] + 1e-2).all()
 
 
+def test_config3_shapes_fp16_sampled():
+    """The N=16384 GQA workload's shapes in fp16 (seed 13), 1,024 rows at tile
+    edges and at random against the oracle, every output finite."""
+    c = dict(workloads.PREFILL_CONFIGS[3])
+    c["dtype"] = "f16"
+    inp = workloads.prefill_inputs(seed=13, **c)
+    print("case: N=16384 Hq=32 Hkv=8 causal fp16, sampled rows", flush=True)
+    o, lse = _run(inp)
+    B, N, Hq, d = inp.q.shape
+    rng = np.random.default_rng(34)
+    edges = np.array([0, 1, 127, 128, 255, 256, 8191, 8192, N - 257, N - 256, N - 2, N - 1])
+    rows = np.array([(0, int(i), h) for h in range(Hq)
+                     for i in np.concatenate([edges, rng.integers(0, N, 20)])])
+    ref, ref_lse = oracle.sdpa_rows(_np(inp.q), _np(inp.k), _np(inp.v), rows, inp.scale, True)
+    ri = torch.from_numpy(rows).to(DEV)
+    assert_close(o[ri[:, 0], ri[:, 1], ri[:, 2]], ref, torch.float16,
+                 "N=16384 fp16 sampled %d rows" % len(rows))
+    assert_lse_close(lse[ri[:, 0], ri[:, 2], ri[:, 1]], ref_lse, torch.float16,
+                     what="N=16384 fp16 sampled lse")
+    assert torch.isfinite(o).all()
+
+
 @pytest.mark.timeout(1200)
 def test_config3_long_causal_gqa_full():
     # every output row and log-sum-exp of the N = 16384 workload against the
