@@ -189,6 +189,10 @@ void attn_fwd_mfma_kernel(FwdParams p) {
       r[j] = lb0 + j < nblk ? ld_meta(p.block_table, (int64_t)b * p.max_blocks_per_seq + lb0 + j) : 0;
     return r;
   };
+  auto tile_ids = [&](int kt) -> i32x4 {
+    if constexpr (PAGED) return tile_blocks(kt);
+    return i32x4{0, 0, 0, 0};
+  };
   auto block_rsrc = [&](const void* cache, int lb, int phys) {
     const char* base = (const char*)cache;
     uint32_t ext = 0;
@@ -200,10 +204,11 @@ void attn_fwd_mfma_kernel(FwdParams p) {
   };
   // Per-lane offsets stay fixed; each tile gets a buffer resource based at its
   // first row (scalar arithmetic) whose extent is what is left of the slice,
-  // so rows past n_k load as zero.
-  auto load_k = [&](int kt, int stage) {
+  // so rows past n_k load as zero.  Paged: `ids` are the tile's block ids
+  // (tile_blocks), read by the caller before the barrier that precedes the
+  // loads, so that the barrier's wait covers the table read.
+  auto load_k = [&](int kt, int stage, const i32x4 ids) {
     if constexpr (PAGED) {
-      const i32x4 ids = tile_blocks(kt);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         // block of this instruction's rows (64 / CPR of them)
@@ -238,9 +243,8 @@ void attn_fwd_mfma_kernel(FwdParams p) {
                      (uint32_t)row * qrowb + (uint32_t)((pc ^ kswz(row)) * 16));
     }
   };
-  auto load_v = [&](int kt, int stage) {
+  auto load_v = [&](int kt, int stage, const i32x4 ids) {
     if constexpr (PAGED) {
-      const i32x4 ids = tile_blocks(kt);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int j = (i * NW + (wave & (NW - 1))) * (64 / CPR) / 16;
@@ -305,8 +309,8 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     // ---- prologue: Q through LDS, K_0 and K_1 staged, S_0 ----
 #pragma unroll
     for (int t = 0; t < QT; ++t) load_q(t);
-    load_k(0, 0);
-    load_k(1, 1);
+    load_k(0, 0, tile_ids(0));
+    load_k(1, 1, tile_ids(1));
     wait_loads_and_sync();
     {
       // this wave's 32 rows sit in Q tile rb / 2, rows 32 (rb % 2) + ...
@@ -343,13 +347,14 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     auto tile = [&](const int kt, auto SC, auto PVC) {
       constexpr int S = decltype(SC)::value;
       constexpr bool PV = decltype(PVC)::value != 0;
+      // K_{kt+2} replaces K_kt (read for S_kt last tile); V_kt replaces
+      // V_{kt-2} (read for its P V last tile)
+      const i32x4 idk = tile_ids(kt + 2), idv = tile_ids(kt);
       // all waves are done with the stage refilled below, and the tiles
       // loaded last time have landed
       if (kt > 0) wait_loads_and_sync();
-      // K_{kt+2} replaces K_kt (read for S_kt last tile); V_kt replaces
-      // V_{kt-2} (read for its P V last tile)
-      load_k(kt + 2, S ^ 1);
-      load_v(kt, S ^ 1);
+      load_k(kt + 2, S ^ 1, idk);
+      load_v(kt, S ^ 1, idv);
       // O holds P_{kt-2} V_{kt-2}: move it to the reference of tile kt-1
       if (PV && pend_grow) {
 #pragma unroll
@@ -518,10 +523,11 @@ void attn_fwd_mfma_kernel(FwdParams p) {
     // (a wave with no visible key starts here at tile 0, which, as for the
     // others, has no barrier: every wave passes the same barriers)
     for (; kt < ntiles; ++kt) {   // tile kt fills stage kt & 1
+      const i32x4 idk = tile_ids(kt + 2), idv = tile_ids(kt);
       if (kt > 0) wait_loads_and_sync();
       if (L >= 0 && kt == L + 1) last_pv(L);
-      load_k(kt + 2, kt & 1);
-      load_v(kt, kt & 1);
+      load_k(kt + 2, kt & 1, idk);
+      load_v(kt, kt & 1, idv);
     }
     wait_loads_and_sync();
     if (L >= 0 && L == ntiles - 1) last_pv(L);
