@@ -308,6 +308,33 @@ def test_validate_rejects_prefix_blocks_that_are_not_shared():
     _rejects(r"block_table\[1\]\[0\] = 3 differs", mutate=mutate)
 
 
+def test_last_error_is_per_thread():
+    """The error message store is per thread: threads that fail concurrently
+    (the validator runs on the host; ctypes releases the interpreter lock
+    during the call) each read their own message."""
+    import threading
+    failures = []
+
+    def worker(t):
+        tab, ctx, gs, pl = _tables()
+        for i in range(300):
+            bad = -(1000 * (t + 1) + i)
+            ctx[2] = bad
+            try:
+                ea.validate_paged_tables(tab, ctx, max_context_len=64, num_blocks=8)
+                failures.append((t, i, "accepted"))
+            except ea.AttnError as e:
+                if "context_lens[2] = %d" % bad not in str(e):
+                    failures.append((t, i, str(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not failures, failures[:5]
+
+
 def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
     # 16 query heads per KV head over 65,535 sequences x 64 KV heads need
     # more workspace than the library's scratch holds: rejected on the host,
